@@ -1,0 +1,294 @@
+"""Plain fp64 CPU oracle of paged KV attention.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  It shares no code with the HIP library
+and never imports it.  Everything here is written for clarity, not speed: it
+follows the definitions the pages give, step by step, in float64.
+
+Sources (page title, section):
+  * Inside vLLM: Anatomy of a High-Throughput LLM Inference System
+    (Gordic; Chinese translation), sections "Engine construction" (per-block
+    byte formula), "Scheduler" (allocate_slots, ceil(n/16) blocks) and
+    "Forward pass" (slot_mapping; one flattened super-sequence with positions
+    and a mask so each sequence sees only its own tokens).
+  * vLLM 技术内幕 (openeuler), section 2.1 (16-token blocks, block table as a
+    page table, blockwise q.k then blockwise value accumulation) and 2.2
+    (ref_cnt and copy-on-write of a shared block on write).
+  * Continuous batching + PagedAttention (juhe.plus), section 3.3 (logical
+    token -> block index and offset -> physical block), 3.6 (the kernel loop
+    over the block table), 3.8 (COW walk-through), 4.2 (chunked prefill).
+  * vLLM 源码精读, sections 2.1-2.4 (block_table, slot_mapping, copy-on-write)
+    and 5.1 (prepare_attn builds slot_mapping; kernels scatter new K/V and
+    gather old K/V through the table).
+
+Readings where the pages are silent (each also listed in the design notes):
+  * slot = physical_block * block_size + offset (implied by the 3.3 example).
+  * a negative slot means "skip this token" (padding).
+  * a sequence's length L counts the tokens written in the current step; the
+    step's K/V are written before attention reads them (3.3 order).
+  * GQA: query head h reads kv head h // (Hq / Hkv).
+  * query i of a sequence with q_len new tokens sits at position
+    L - q_len + i and sees keys 0..position (causal).
+  * a freed block returns to the head of the free list; a request's blocks are
+    returned last-to-first (vLLM 技术内幕 3.1 and 4: tail-to-head return,
+    unhashed blocks reused first).
+
+Pool layout (this library's documented ABI; the oracle implements it with
+its own index arithmetic):
+  pool[num_blocks][num_kv_heads][2 (K, V)][tile], tile = block_size*head_size
+  elements.  With E = 16 / dtype_bytes elements per 16-byte granule:
+    K tile: element (t, d) at ((d // E) * block_size + t) * E + d % E
+    V tile: element (t, d) at ((t // E) * head_size + d) * E + t % E
+"""
+from __future__ import annotations
+
+import math
+from collections import deque
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+# ----------------------------------------------------------------------------
+# element types: codes are the raw stored bit patterns
+# ----------------------------------------------------------------------------
+_CODE = {"f32": np.uint32, "bf16": np.uint16}
+_BYTES = {"f32": 4, "bf16": 2}
+
+
+def code_dtype(dtype: str):
+    return _CODE[dtype]
+
+
+def dtype_bytes(dtype: str) -> int:
+    return _BYTES[dtype]
+
+
+def decode(codes: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact value of stored codes, as float64 (bf16 is the top half of an
+    IEEE binary32, so widening is exact)."""
+    if dtype == "bf16":
+        return (codes.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.ascontiguousarray(codes).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# sizes (Inside vLLM, "Engine construction": 2 * block_size * num_kv_heads *
+# head_size * dtype_bytes per block and layer)
+# ----------------------------------------------------------------------------
+def block_bytes(block_size: int, num_kv_heads: int, head_size: int, dtype_nbytes: int) -> int:
+    return 2 * block_size * num_kv_heads * head_size * dtype_nbytes
+
+
+def blocks_for_tokens(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    """Inside vLLM, "Scheduler": n tokens need ceil(n / block_size) blocks."""
+    return -(-n_tokens // block_size)
+
+
+# ----------------------------------------------------------------------------
+# pool layout
+# ----------------------------------------------------------------------------
+def _granule(dtype: str) -> int:
+    return 16 // dtype_bytes(dtype)
+
+
+def k_tile_index(head_size: int, dtype: str, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """[block_size][head_size] -> flat position inside a K tile."""
+    E = _granule(dtype)
+    t = np.arange(block_size)[:, None]
+    d = np.arange(head_size)[None, :]
+    return ((d // E) * block_size + t) * E + (d % E)
+
+
+def v_tile_index(head_size: int, dtype: str, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """[block_size][head_size] -> flat position inside a V tile."""
+    E = _granule(dtype)
+    t = np.arange(block_size)[:, None]
+    d = np.arange(head_size)[None, :]
+    return ((t // E) * head_size + d) * E + (t % E)
+
+
+def new_pool(num_blocks: int, num_kv_heads: int, head_size: int, dtype: str,
+             fill_code: int, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """A pool of codes, every element set to ``fill_code``."""
+    return np.full((num_blocks, num_kv_heads, 2, block_size * head_size), fill_code,
+                   dtype=code_dtype(dtype))
+
+
+# ----------------------------------------------------------------------------
+# address translation (juhe.plus 3.3: token -> (pos // bs, pos % bs) -> physical)
+# ----------------------------------------------------------------------------
+def slot_of(table_row, pos: int, block_size: int = BLOCK_SIZE) -> int:
+    logical_block, offset = divmod(int(pos), block_size)
+    return int(table_row[logical_block]) * block_size + offset
+
+
+def slot_mapping(block_tables: np.ndarray, query_start_loc: np.ndarray,
+                 seq_lens: np.ndarray, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Slots of the step's new tokens, in flattened token order (vLLM 源码精读
+    5.1: prepare_attn maps every new token's logical position to its slot)."""
+    out = []
+    for s in range(len(seq_lens)):
+        q_len = int(query_start_loc[s + 1] - query_start_loc[s])
+        L = int(seq_lens[s])
+        for i in range(q_len):
+            out.append(slot_of(block_tables[s], L - q_len + i, block_size))
+    return np.asarray(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------
+# block allocator with reference counts and copy-on-write
+# (Inside vLLM "Scheduler": allocate_slots pops the first n free blocks;
+#  vLLM 技术内幕 2.2 and juhe.plus 3.8: writing into a block whose ref_cnt > 1
+#  allocates a new block, copies, and drops one reference of the old one)
+# ----------------------------------------------------------------------------
+class CowPool:
+    def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK_SIZE):
+        self.block_size = block_size
+        order = range(num_blocks) if free_order is None else [int(b) for b in free_order]
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def _pop(self) -> int:
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    def append(self, table: list, cur_len: int, n_new: int):
+        """Make room for n_new tokens after cur_len cached ones.
+
+        ``table`` (a Python list of physical ids, one per logical block) is
+        updated in place.  Returns (slots of the new tokens, cow pair or None).
+        """
+        bs = self.block_size
+        have = blocks_for_tokens(cur_len, bs)
+        need = blocks_for_tokens(cur_len + n_new, bs)
+        assert len(table) == have
+        cow = None
+        partial = (cur_len % bs) != 0 and n_new > 0
+        extra = need - have + (1 if partial and self.ref[table[-1]] > 1 else 0)
+        if extra > len(self.free):
+            raise MemoryError("pool exhausted")
+        if partial and self.ref[table[-1]] > 1:
+            old = table[-1]
+            new = self._pop()
+            self.ref[old] -= 1
+            table[-1] = new
+            cow = (old, new)
+        for _ in range(need - have):
+            table.append(self._pop())
+        slots = [slot_of(table, cur_len + i, bs) for i in range(n_new)]
+        return slots, cow
+
+    def fork(self, table: list) -> list:
+        """Another holder of the same blocks (parallel sampling, juhe.plus 3.5)."""
+        for b in table:
+            self.ref[b] += 1
+        return list(table)
+
+    def release(self, table: list) -> None:
+        """Drop one reference of each block, last block first; a block whose
+        count reaches zero goes to the head of the free list."""
+        for b in reversed(table):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free.appendleft(b)
+        table.clear()
+
+
+# ----------------------------------------------------------------------------
+# the two data movements
+# ----------------------------------------------------------------------------
+def kv_write(pool: np.ndarray, dtype: str, k_new: np.ndarray, v_new: np.ndarray,
+             slots, block_size: int = BLOCK_SIZE) -> None:
+    """Scatter each new token's K and V rows (all kv heads) to its slot, in
+    place (vLLM 技术内幕 2.1: write_to_paged_cache / reshape_and_cache).
+    k_new, v_new: codes [T][Hkv][D].  A negative slot is skipped."""
+    D = k_new.shape[2]
+    kidx = k_tile_index(D, dtype, block_size)
+    vidx = v_tile_index(D, dtype, block_size)
+    for t, slot in enumerate(slots):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        blk, off = divmod(slot, block_size)
+        pool[blk, :, 0, kidx[off]] = k_new[t].T   # fancy index is [D][Hkv]
+        pool[blk, :, 1, vidx[off]] = v_new[t].T
+
+
+def block_copy(pool: np.ndarray, pairs) -> None:
+    """For every (src, dst): block dst becomes a copy of block src as it was
+    before the call (juhe.plus 3.8: copy block 2 into the new block 7)."""
+    snapshot = {int(s): pool[int(s)].copy() for s, _ in pairs}
+    for s, d in pairs:
+        pool[int(d)] = snapshot[int(s)]
+
+
+# ----------------------------------------------------------------------------
+# attention
+# ----------------------------------------------------------------------------
+def gather_kv(pool: np.ndarray, dtype: str, table_row, L: int, head_size: int,
+              block_size: int = BLOCK_SIZE):
+    """Codes K, V [L][Hkv][D] of one sequence, walking its block table in
+    logical order (juhe.plus 3.6: look up the physical block, read its K/V)."""
+    kidx = k_tile_index(head_size, dtype, block_size)
+    vidx = v_tile_index(head_size, dtype, block_size)
+    Hkv = pool.shape[1]
+    K = np.empty((L, Hkv, head_size), dtype=pool.dtype)
+    V = np.empty((L, Hkv, head_size), dtype=pool.dtype)
+    for j in range(L):
+        blk = int(table_row[j // block_size])
+        off = j % block_size
+        K[j] = pool[blk, :, 0, kidx[off]].T
+        V[j] = pool[blk, :, 1, vidx[off]].T
+    return K, V
+
+
+def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions, scale: float) -> np.ndarray:
+    """Textbook softmax attention of query rows over one sequence's history.
+
+    q: float64 [n][Hq][D]; K, V: float64 [L][Hkv][D]; positions[i] is the
+    absolute position of query row i, which sees keys 0..positions[i].
+    Returns float64 [n][Hq][D].
+    """
+    n, Hq, D = q.shape
+    Hkv = K.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((n, Hq, D), dtype=np.float64)
+    for i in range(n):
+        p = int(positions[i])
+        for h in range(Hq):
+            g = h // group
+            x = scale * (K[: p + 1, g, :] @ q[i, h, :])
+            w = np.exp(x - x.max())
+            out[i, h, :] = (w @ V[: p + 1, g, :]) / w.sum()
+    return out
+
+
+def paged_attention(pool: np.ndarray, dtype: str, q_codes: np.ndarray, block_tables,
+                    seq_lens, query_start_loc, scale: float,
+                    block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """Attention of a flattened batch of query rows over the paged cache.
+
+    q_codes: codes [T][Hq][D]; sequence s owns rows
+    query_start_loc[s] .. query_start_loc[s+1]-1 (Inside vLLM "Forward pass":
+    one super-sequence, each sequence attending only to its own tokens).
+    A sequence of length 0 yields zeros.  Returns float64 [T][Hq][D].
+    """
+    T, Hq, D = q_codes.shape
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    q = decode(q_codes, dtype)
+    for s in range(len(seq_lens)):
+        L = int(seq_lens[s])
+        r0, r1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
+        if L == 0 or r1 == r0:
+            continue
+        K, V = gather_kv(pool, dtype, block_tables[s], L, D, block_size)
+        positions = [L - (r1 - r0) + i for i in range(r1 - r0)]
+        out[r0:r1] = attention_rows(q[r0:r1], decode(K, dtype), decode(V, dtype), positions, scale)
+    return out

@@ -1,0 +1,328 @@
+"""Pins of the CPU oracle against what the pages print and what mathematics
+fixes.  None of these calls the HIP library."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import paged_oracle as po
+from oracle import scenario
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_examples.json")))
+
+
+def _rand_codes(rng, shape, dtype):
+    if dtype == "f32":
+        return rng.uniform(-1, 1, size=shape).astype(np.float32).view(np.uint32)
+    return workloads._bf16_codes(rng.standard_normal(shape).astype(np.float32))
+
+
+# ---------------------------------------------------------------- page values
+def test_byte_formula_13b_per_token():
+    g = GOLD["kv_bytes_per_token_13b"]
+    per_block = po.block_bytes(g["block_size"], g["num_kv_heads"], g["head_size"], g["dtype_bytes"])
+    per_token = g["layers"] * per_block // g["block_size"]
+    assert per_token == 819_200                      # 800 KiB
+    assert abs(per_token / 1000 - g["per_token_kb_approx"]) / g["per_token_kb_approx"] < 0.03
+    total = per_token * g["tokens"]
+    assert abs(total / 1e9 - g["total_gb_approx"]) / g["total_gb_approx"] < 0.06
+
+
+@pytest.mark.parametrize("cfg,expected", [(1, 32_768), (2, 262_144), (3, 65_536), (4, 65_536), (5, 327_680)])
+def test_pool_bytes_match_page_formula(cfg, expected):
+    w = workloads.small(cfg)
+    pool = po.new_pool(3, w.num_kv_heads, w.head_size, w.dtype, 0)
+    assert pool.nbytes // 3 == expected
+    assert po.block_bytes(16, w.num_kv_heads, w.head_size, w.dtype_bytes) == expected
+
+
+def test_block_count_rule():
+    g = GOLD["block_count"]
+    assert po.blocks_for_tokens(g["new_tokens"]) == g["blocks"]
+    alloc = po.CowPool(8)
+    table = []
+    alloc.append(table, 0, g["new_tokens"])
+    assert len(table) == g["blocks"]
+    # the 17th token starts a fresh block at offset 0
+    t2 = []
+    s2, _ = po.CowPool(8).append(t2, 0, 17)
+    assert s2[16] % 16 == 0 and s2[16] // 16 == t2[1]
+
+
+def test_address_translation_example():
+    g = GOLD["address_translation"]
+    slot = po.slot_of(g["block_table"] + [99], g["token"])
+    assert divmod(slot, 16) == (g["physical_block"], g["offset"])
+    assert g["token"] // 16 == g["logical_block"]
+
+
+def test_copy_on_write_walkthrough():
+    g = GOLD["copy_on_write"]
+    # free list arranged so the prompt gets 0,1,2 and the next free block is 7
+    alloc = po.CowPool(10, free_order=[0, 1, 2, 7, 3, 4, 5, 6, 8, 9])
+    prompt = []
+    alloc.append(prompt, 0, 40)                     # 3 blocks, last one partly filled
+    assert prompt == g["prompt_blocks"]
+    samples = [prompt] + [alloc.fork(prompt) for _ in range(g["samples"] - 1)]
+    assert [alloc.ref[b] for b in prompt] == g["refs_after_fork"]
+    slots, cow = alloc.append(samples[0], 40, 1)
+    assert cow == tuple(g["copy"])
+    assert samples[0] == g["table_after"]
+    assert alloc.ref[2] == g["ref_of_old_after"]
+    assert slots == [7 * 16 + 40 % 16]
+    # the rule: only a shared block is copied; the last holder writes in place
+    for s in samples[1:3]:
+        _, c = alloc.append(s, 40, 1)
+        assert c is not None and c[0] == 2
+    assert alloc.ref[2] == 1
+    _, c = alloc.append(samples[3], 40, 1)
+    assert c is None and samples[3][-1] == 2
+
+
+def test_chunked_prefill_step_shape():
+    g = GOLD["chunked_prefill_step"]
+    assert g["budget"] - g["decodes"] == g["chunk"]
+    w = workloads.make(4)
+    assert w.num_tokens == 2048                     # the 2048-token budget
+    assert int(w.q_len.max()) == 1950 and int((w.q_len == 1).sum()) == 98
+
+
+# ---------------------------------------------------------------- allocator
+def test_release_order_and_reuse():
+    alloc = po.CowPool(6, free_order=[5, 4, 3, 2, 1, 0])
+    t = []
+    alloc.append(t, 0, 33)                          # 3 blocks: 5, 4, 3
+    assert t == [5, 4, 3]
+    alloc.release(t)
+    assert list(alloc.free)[:3] == [5, 4, 3]        # returned last-first to the head
+    t2 = []
+    alloc.append(t2, 0, 1)
+    assert t2 == [5]
+
+
+def test_pool_exhaustion_raises():
+    alloc = po.CowPool(2)
+    t = []
+    with pytest.raises(MemoryError):
+        alloc.append(t, 0, 33)
+
+
+def test_slot_mapping_agrees_with_allocator():
+    w = workloads.small(4)
+    st = scenario.build_tables(w, with_pool=False)
+    bt = scenario.table_matrix(st["tables"])
+    assert np.array_equal(po.slot_mapping(bt, w.query_start_loc, w.seq_lens), st["slots"])
+
+
+# ---------------------------------------------------------------- data movement
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layout_offsets(dtype):
+    """Every element lands at the offset the documented layout gives, computed
+    here one element at a time from byte arithmetic."""
+    rng = np.random.default_rng(1)
+    Hkv, D, nb = 2, 64, 5
+    es = po.dtype_bytes(dtype)
+    E = 16 // es
+    pool = po.new_pool(nb, Hkv, D, dtype, 0)
+    k = rng.integers(1, 2 ** (8 * es) - 1, size=(1, Hkv, D)).astype(po.code_dtype(dtype))
+    v = rng.integers(1, 2 ** (8 * es) - 1, size=(1, Hkv, D)).astype(po.code_dtype(dtype))
+    blk, off = 3, 11
+    po.kv_write(pool, dtype, k, v, [blk * 16 + off])
+    raw = pool.view(np.uint8).reshape(-1)
+    blk_bytes = 2 * 16 * Hkv * D * es
+    for h in range(Hkv):
+        for d in range(D):
+            kb = blk * blk_bytes + h * 2 * 16 * D * es + ((d // E) * 16 + off) * 16 + (d % E) * es
+            vb = (blk * blk_bytes + h * 2 * 16 * D * es + 16 * D * es
+                  + ((off // E) * D + d) * 16 + (off % E) * es)
+            assert raw[kb:kb + es].view(po.code_dtype(dtype))[0] == k[0, h, d]
+            assert raw[vb:vb + es].view(po.code_dtype(dtype))[0] == v[0, h, d]
+    assert np.count_nonzero(pool) == 2 * Hkv * D
+
+
+def test_kv_write_skip_and_untouched():
+    rng = np.random.default_rng(2)
+    pool = po.new_pool(4, 2, 64, "bf16", workloads.BF16_NAN)
+    before = pool.copy()
+    k = _rand_codes(rng, (3, 2, 64), "bf16")
+    v = _rand_codes(rng, (3, 2, 64), "bf16")
+    po.kv_write(pool, "bf16", k, v, [5, -1, 63])
+    K, V = po.gather_kv(pool, "bf16", [0, 1, 2, 3], 64, 64)
+    assert np.array_equal(K[5], k[0]) and np.array_equal(V[63], v[2])
+    changed = np.argwhere((pool != before).any(axis=(1, 2, 3))).ravel().tolist()
+    assert changed == [0, 3]
+    untouched_rows = [j for j in range(64) if j not in (5, 63)]
+    assert np.all(K[untouched_rows] == workloads.BF16_NAN)
+
+
+def test_block_copy_reads_pre_call_contents():
+    rng = np.random.default_rng(3)
+    pool = _rand_codes(rng, (6, 2, 2, 16 * 64), "bf16")
+    snap = pool.copy()
+    po.block_copy(pool, [(1, 4), (1, 5), (2, 0)])
+    assert np.array_equal(pool[4], snap[1]) and np.array_equal(pool[5], snap[1])
+    assert np.array_equal(pool[0], snap[2])
+    assert np.array_equal(pool[[1, 2, 3]], snap[[1, 2, 3]])
+
+
+# ---------------------------------------------------------------- attention
+def _dense_attention_einsum(q, K, V, positions, scale, group):
+    """A second, differently written textbook attention on dense arrays."""
+    Kx = np.repeat(K, group, axis=1)                # [L][Hq][D]
+    Vx = np.repeat(V, group, axis=1)
+    s = np.einsum("nhd,lhd->nhl", q, Kx) * scale
+    L = K.shape[0]
+    mask = np.arange(L)[None, None, :] > np.asarray(positions)[:, None, None]
+    s = np.where(mask, -np.inf, s)
+    s = s - s.max(axis=2, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=2, keepdims=True)
+    return np.einsum("nhl,lhd->nhd", p, Vx)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_paged_equals_contiguous(cfg):
+    w = workloads.small(cfg)
+    st = scenario.run_step(w)
+    qsl = w.query_start_loc
+    G = w.num_q_heads // w.num_kv_heads
+    for s in range(w.batch):
+        K, V = scenario.sequence_kv(w, s)
+        L = int(w.seq_lens[s])
+        q_len = int(w.q_len[s])
+        q = po.decode(w.q[qsl[s]:qsl[s + 1]], w.dtype)
+        ref = _dense_attention_einsum(q, po.decode(K, w.dtype), po.decode(V, w.dtype),
+                                      [L - q_len + i for i in range(q_len)], w.scale, G)
+        np.testing.assert_allclose(st["out"][qsl[s]:qsl[s + 1]], ref, rtol=0, atol=1e-13)
+
+
+def test_torch_sdpa_matches_mixed_step():
+    """The library routine: PyTorch's scaled_dot_product_attention in float64
+    with an explicit causal-with-offset mask and GQA-expanded heads."""
+    w = workloads.small(4)
+    st = scenario.run_step(w)
+    qsl = w.query_start_loc
+    G = w.num_q_heads // w.num_kv_heads
+    for s in range(w.batch):
+        K, V = scenario.sequence_kv(w, s)
+        L, q_len = int(w.seq_lens[s]), int(w.q_len[s])
+        q = torch.from_numpy(po.decode(w.q[qsl[s]:qsl[s + 1]], w.dtype)).permute(1, 0, 2)
+        k = torch.from_numpy(po.decode(K, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        v = torch.from_numpy(po.decode(V, w.dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+        pos = torch.arange(L - q_len, L)[:, None]
+        mask = torch.arange(L)[None, :] <= pos
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=w.scale)
+        np.testing.assert_allclose(st["out"][qsl[s]:qsl[s + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_block_permutation_invariance():
+    """Moving every block to another physical id and rewriting the tables
+    leaves the output bit-identical."""
+    w = workloads.small(3)
+    st = scenario.run_step(w)
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(w.num_blocks)
+    pool2 = np.empty_like(st["pool"])
+    pool2[perm] = st["pool"]
+    bt2 = perm[st["block_tables"]].astype(np.int32)
+    out2 = po.paged_attention(pool2, w.dtype, w.q, bt2, w.seq_lens, w.query_start_loc, w.scale)
+    assert np.array_equal(out2, st["out"])
+
+
+def test_brute_force_tiny_decode():
+    """Config 1 recomputed with scalar Python loops and math.exp."""
+    w = workloads.make(1)
+    st = scenario.run_step(w)
+    qsl = w.query_start_loc
+    for s in range(w.batch):
+        K, V = scenario.sequence_kv(w, s)
+        Kf, Vf = po.decode(K, "f32"), po.decode(V, "f32")
+        L = int(w.seq_lens[s])
+        qrow = po.decode(w.q[qsl[s]], "f32")
+        for h in range(w.num_q_heads):
+            xs = [w.scale * sum(qrow[h, d] * Kf[j, h, d] for d in range(w.head_size)) for j in range(L)]
+            mx = max(xs)
+            ws = [math.exp(x - mx) for x in xs]
+            tot = sum(ws)
+            o = [sum(ws[j] * Vf[j, h, d] for j in range(L)) / tot for d in range(w.head_size)]
+            np.testing.assert_allclose(st["out"][qsl[s], h], o, rtol=0, atol=1e-13)
+
+
+def test_closed_form_single_key():
+    rng = np.random.default_rng(4)
+    pool = po.new_pool(2, 1, 64, "bf16", workloads.BF16_NAN)
+    k = _rand_codes(rng, (1, 1, 64), "bf16")
+    v = _rand_codes(rng, (1, 1, 64), "bf16")
+    po.kv_write(pool, "bf16", k, v, [16])
+    q = _rand_codes(rng, (1, 2, 64), "bf16")
+    out = po.paged_attention(pool, "bf16", q, np.array([[1]]), [1], [0, 1], 0.125)
+    assert np.array_equal(out[0, 0], po.decode(v[0, 0], "bf16"))
+    assert np.array_equal(out[0, 1], po.decode(v[0, 0], "bf16"))
+
+
+def test_closed_form_zero_query_is_mean():
+    rng = np.random.default_rng(5)
+    L = 37
+    pool = po.new_pool(4, 2, 64, "f32", workloads.F32_NAN)
+    k = _rand_codes(rng, (L, 2, 64), "f32")
+    v = _rand_codes(rng, (L, 2, 64), "f32")
+    po.kv_write(pool, "f32", k, v, [16 * [2, 0, 3][j // 16] + j % 16 for j in range(L)])
+    q = np.zeros((1, 2, 64), np.uint32)
+    out = po.paged_attention(pool, "f32", q, np.array([[2, 0, 3]]), [L], [0, 1], 1.0)
+    np.testing.assert_allclose(out[0], po.decode(v, "f32").mean(axis=0), rtol=0, atol=1e-15)
+
+
+def test_closed_form_dominant_key():
+    rng = np.random.default_rng(6)
+    L = 20
+    pool = po.new_pool(2, 1, 64, "f32", workloads.F32_NAN)
+    k = np.zeros((L, 1, 64), np.float32)
+    k[13, 0, :] = 1.0
+    v = _rand_codes(rng, (L, 1, 64), "f32")
+    po.kv_write(pool, "f32", k.view(np.uint32), v, list(range(L)))
+    q = np.full((1, 1, 64), 1.0, np.float32).view(np.uint32)
+    out = po.paged_attention(pool, "f32", q, np.array([[0, 1]]), [L], [0, 1], 10.0)
+    # weight of key 13 is 1 / (1 + 19 e^-640) == 1 in float64
+    assert np.array_equal(out[0, 0], po.decode(v[13, 0], "f32"))
+
+
+def test_causal_rows_see_only_their_prefix():
+    """Changing a key after position p must not change query rows at <= p."""
+    w = workloads.small(4)
+    st = scenario.run_step(w)
+    s = w.batch - 1                                 # the prefill chunk
+    bt = st["block_tables"]
+    L = int(w.seq_lens[s])
+    pool2 = st["pool"].copy()
+    blk = bt[s][(L - 1) // 16]
+    pool2[blk, :, :, :] = workloads.BF16_NAN       # poison the last block
+    out2 = po.paged_attention(pool2, w.dtype, w.q, bt, w.seq_lens, w.query_start_loc, w.scale)
+    first_poisoned = ((L - 1) // 16) * 16
+    q_len = int(w.q_len[s])
+    r0 = int(w.query_start_loc[s])
+    for i in range(q_len):
+        pos = L - q_len + i
+        same = np.array_equal(out2[r0 + i], st["out"][r0 + i])
+        assert same == (pos < first_poisoned)
+
+
+def test_empty_sequence_gives_zeros():
+    pool = po.new_pool(2, 1, 64, "bf16", workloads.BF16_NAN)
+    q = np.zeros((1, 1, 64), np.uint16)
+    out = po.paged_attention(pool, "bf16", q, np.array([[0]]), [0], [0, 1], 0.125)
+    assert np.all(out == 0)
+
+
+def test_config5_forks_all_copy_on_write():
+    w = workloads.small(5)
+    st = scenario.build_tables(w, with_pool=False)
+    n_fork = int((w.fork_of >= 0).sum())
+    assert len(st["cow_pairs"]) == n_fork
+    shared_last = st["prompt_tables"][0][-1]
+    assert all(int(p[0]) == shared_last for p in st["cow_pairs"])
+    assert st["alloc"].ref[shared_last] == 1        # only the owner holds it now

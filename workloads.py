@@ -1,0 +1,237 @@
+"""Seeded synthetic workloads shaped like the pages' serving workloads.
+
+This module only *draws* inputs: sequence lengths, the order in which the
+pool hands out physical blocks, and K/V/Q values.  It holds none of the
+method's arithmetic (no slot, table, copy or attention computation): the HIP
+library and the CPU oracle each derive those from what is drawn here.
+
+Five workloads, all with 16-token blocks:
+  1 tiny decode      4 seqs, L = {5,16,17,40}, Hq = Hkv = 4, D = 64, fp32
+                     U[-1,1], pool of 64 blocks handed out in a seeded random
+                     order, scale 1/8.
+  2 7B-shaped MHA    Hq = Hkv = 32, D = 128, bf16 N(0,1), B = 64,
+                     L ~ U[128, 2048], pool = 1.25 x the blocks needed.
+  3 8B-shaped GQA    Hq = 32, Hkv = 8, D = 128, bf16 N(0,1), B = 256,
+                     L ~ lognormal(median 800, sigma 1) clipped to [16, 8192],
+                     blocks scattered over a pool of 200,000.
+  4 mixed step       8B GQA shape; 98 decode seqs (L ~ U[64, 4096]) followed
+                     by one 1950-token prefill chunk on top of 1048 cached
+                     tokens; 2048 new tokens in all.
+  5 13B-shaped MHA   Hq = Hkv = 40, D = 128, bf16; 16 forks of one
+                     1032-token prompt (the prompt's owner keeps a reference),
+                     16 independent seqs with L ~ U[1, 16384], one at 16384.
+
+Every sequence appends ``q_len`` new tokens in the step (1 for decode) on
+top of ``hist_len`` cached ones, so its length is hist_len + q_len.
+
+Random streams: numpy SeedSequence(config_id + 1000 * seed).spawn(4) ->
+(lengths, physical block order, values, spare).  Values are drawn in float32
+and rounded to nearest-even bf16 where the workload is bf16.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_SIZE = 16
+BF16_NAN = 0x7FC0
+F32_NAN = 0x7FC00000
+
+
+@dataclass
+class Workload:
+    config_id: int
+    name: str
+    dtype: str                  # "f32" | "bf16"
+    num_q_heads: int
+    num_kv_heads: int
+    head_size: int
+    scale: float
+    num_blocks: int             # pool size in blocks
+    free_order: np.ndarray      # int32 [num_blocks]: order the pool hands out blocks
+    hist_len: np.ndarray        # int32 [B]: tokens cached before the step
+    q_len: np.ndarray           # int32 [B]: tokens appended (and queried) in the step
+    fork_of: np.ndarray         # int32 [B]: -1, or index of the shared prompt it forks
+    prompt_len: np.ndarray      # int32 [P]: lengths of shared prompts
+    prompt_owner_keeps_ref: bool
+    # codes (uint16 for bf16, uint32 for f32)
+    hist_k: np.ndarray          # [sum hist of independent seqs][Hkv][D]
+    hist_v: np.ndarray
+    hist_start: np.ndarray      # int64 [B+1] offsets into hist_* (forks own none)
+    prompt_k: np.ndarray        # [sum prompt_len][Hkv][D]
+    prompt_v: np.ndarray
+    prompt_start: np.ndarray    # int64 [P+1]
+    new_k: np.ndarray           # [T][Hkv][D], T = sum q_len, flattened seq order
+    new_v: np.ndarray
+    q: np.ndarray               # [T][Hq][D]
+    pool_fill: int              # code every pool element holds before use (NaN)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return int(self.hist_len.shape[0])
+
+    @property
+    def seq_lens(self) -> np.ndarray:
+        return (self.hist_len + self.q_len).astype(np.int32)
+
+    @property
+    def query_start_loc(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.q_len)]).astype(np.int32)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.q_len.sum())
+
+    @property
+    def dtype_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+
+def _bf16_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 codes, round to nearest even (inputs are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32).view(np.uint32)
+    out = np.empty(shape, dtype=np.uint16)
+    flat = out.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat.size, step):
+        n = min(step, flat.size - i)
+        flat[i:i + n] = _bf16_codes(rng.standard_normal(n, dtype=np.float32))
+    return out
+
+
+def _pool_size(lengths, factor: float, extra_blocks: int = 0) -> int:
+    need = int(sum((int(L) + BLOCK_SIZE - 1) // BLOCK_SIZE for L in lengths)) + extra_blocks
+    return int(np.ceil(factor * need))
+
+
+def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, scale: float,
+           hist_len, q_len, num_blocks: int, streams, fork_of=None, prompt_len=(),
+           owner_ref=False, extra=None) -> Workload:
+    _, r_blocks, r_vals, _ = streams
+    hist_len = np.asarray(hist_len, dtype=np.int32)
+    q_len = np.asarray(q_len, dtype=np.int32)
+    B = hist_len.shape[0]
+    fork_of = np.full(B, -1, np.int32) if fork_of is None else np.asarray(fork_of, np.int32)
+    prompt_len = np.asarray(prompt_len, dtype=np.int32)
+    own_hist = np.where(fork_of < 0, hist_len, 0).astype(np.int64)
+    hist_start = np.concatenate([[0], np.cumsum(own_hist)]).astype(np.int64)
+    prompt_start = np.concatenate([[0], np.cumsum(prompt_len.astype(np.int64))]).astype(np.int64)
+    free_order = r_blocks.permutation(num_blocks).astype(np.int32)
+    T = int(q_len.sum())
+    n_hist = int(hist_start[-1])
+    n_prompt = int(prompt_start[-1])
+    w = Workload(
+        config_id=config_id, name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv,
+        head_size=D, scale=scale, num_blocks=num_blocks, free_order=free_order,
+        hist_len=hist_len, q_len=q_len, fork_of=fork_of, prompt_len=prompt_len,
+        prompt_owner_keeps_ref=owner_ref,
+        hist_k=_values(r_vals, (n_hist, Hkv, D), dtype),
+        hist_v=_values(r_vals, (n_hist, Hkv, D), dtype),
+        hist_start=hist_start,
+        prompt_k=_values(r_vals, (n_prompt, Hkv, D), dtype),
+        prompt_v=_values(r_vals, (n_prompt, Hkv, D), dtype),
+        prompt_start=prompt_start,
+        new_k=_values(r_vals, (T, Hkv, D), dtype),
+        new_v=_values(r_vals, (T, Hkv, D), dtype),
+        q=_values(r_vals, (T, Hq, D), dtype),
+        pool_fill=F32_NAN if dtype == "f32" else BF16_NAN,
+        extra=extra or {},
+    )
+    return w
+
+
+def make(config_id: int, seed: int = 0, batch: int | None = None) -> Workload:
+    """The workload of one configuration.  ``batch`` (optional) keeps the
+    shape and length distribution but draws fewer sequences, for quick runs."""
+    streams = np.random.SeedSequence(config_id + 1000 * seed).spawn(4)
+    streams = [np.random.default_rng(s) for s in streams]
+    r_len = streams[0]
+
+    if config_id == 1:
+        L = np.array([5, 16, 17, 40], np.int32)
+        return _build(1, "tiny decode", "f32", 4, 4, 64, 1.0 / 8.0, L - 1, np.ones(4, np.int32),
+                      64, streams)
+
+    if config_id == 2:
+        B = batch or 64
+        L = r_len.integers(128, 2048, size=B, endpoint=True).astype(np.int32)
+        return _build(2, "7B MHA decode", "bf16", 32, 32, 128, 128 ** -0.5, L - 1,
+                      np.ones(B, np.int32), _pool_size(L, 1.25), streams)
+
+    if config_id == 3:
+        B = batch or 256
+        L = np.rint(r_len.lognormal(np.log(800.0), 1.0, size=B))
+        L = np.clip(L, 16, 8192).astype(np.int32)
+        return _build(3, "8B GQA decode", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                      np.ones(B, np.int32), 200_000, streams)
+
+    if config_id == 4:
+        n_dec = 98 if batch is None else max(batch - 1, 1)
+        L_dec = r_len.integers(64, 4096, size=n_dec, endpoint=True).astype(np.int32)
+        chunk, cached = 1950, 1048
+        hist = np.concatenate([L_dec - 1, [cached]]).astype(np.int32)
+        qlen = np.concatenate([np.ones(n_dec, np.int32), [chunk]]).astype(np.int32)
+        return _build(4, "mixed chunked prefill + decode", "bf16", 32, 8, 128, 128 ** -0.5,
+                      hist, qlen, _pool_size(hist + qlen, 1.25), streams)
+
+    if config_id == 5:
+        n_fork = 16 if batch is None else max(batch // 2, 1)
+        n_ind = 16 if batch is None else max(batch - n_fork, 1)
+        prompt = 1032
+        L_ind = r_len.integers(1, 16384, size=n_ind, endpoint=True).astype(np.int32)
+        L_ind[0] = 16384
+        hist = np.concatenate([np.full(n_fork, prompt, np.int32), L_ind - 1]).astype(np.int32)
+        qlen = np.ones(n_fork + n_ind, np.int32)
+        fork_of = np.concatenate([np.zeros(n_fork, np.int32), np.full(n_ind, -1, np.int32)])
+        lengths = list(L_ind) + [prompt]
+        return _build(5, "13B MHA prefix sharing + long context", "bf16", 40, 40, 128,
+                      128 ** -0.5, hist, qlen, _pool_size(lengths, 1.25, extra_blocks=n_fork),
+                      streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True)
+
+    raise ValueError(f"unknown config {config_id}")
+
+
+def small(config_id: int, seed: int = 0) -> Workload:
+    """A reduced workload of the same family that the oracle finishes in
+    seconds: same head shapes and distributions, fewer and shorter seqs."""
+    streams = [np.random.default_rng(s)
+               for s in np.random.SeedSequence(10_000 + config_id + 1000 * seed).spawn(4)]
+    r_len = streams[0]
+    if config_id == 1:
+        return make(1, seed)
+    if config_id == 2:
+        L = r_len.integers(1, 300, size=6, endpoint=True).astype(np.int32)
+        return _build(2, "7B MHA decode (small)", "bf16", 32, 32, 128, 128 ** -0.5, L - 1,
+                      np.ones(6, np.int32), _pool_size(L, 1.25), streams)
+    if config_id == 3:
+        L = np.clip(np.rint(r_len.lognormal(np.log(120.0), 1.0, size=12)), 1, 900).astype(np.int32)
+        L[0] = 1
+        L[1] = 16
+        L[2] = 17
+        L[3] = 513
+        return _build(3, "8B GQA decode (small)", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                      np.ones(12, np.int32), 4000, streams)
+    if config_id == 4:
+        L_dec = r_len.integers(1, 400, size=5, endpoint=True).astype(np.int32)
+        hist = np.concatenate([L_dec - 1, [37]]).astype(np.int32)
+        qlen = np.concatenate([np.ones(5, np.int32), [150]]).astype(np.int32)
+        return _build(4, "mixed step (small)", "bf16", 32, 8, 128, 128 ** -0.5, hist, qlen,
+                      _pool_size(hist + qlen, 1.25), streams)
+    if config_id == 5:
+        prompt = 40
+        L_ind = r_len.integers(1, 600, size=3, endpoint=True).astype(np.int32)
+        hist = np.concatenate([np.full(3, prompt, np.int32), L_ind - 1]).astype(np.int32)
+        fork_of = np.array([0, 0, 0, -1, -1, -1], np.int32)
+        return _build(5, "13B MHA prefix sharing (small)", "bf16", 40, 40, 128, 128 ** -0.5,
+                      hist, np.ones(6, np.int32), _pool_size(list(L_ind) + [prompt], 1.25, 3),
+                      streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True)
+    raise ValueError(config_id)
