@@ -1,0 +1,167 @@
+"""Benchmark of the paged KV attention hot path on one MI355X.
+
+A step is one pass of the whole path over the 8B-shaped GQA decode batch
+(32 query / 8 kv heads, head size 128, bf16, 256 sequences with lognormal
+contexts, median 800, in a 200,000-block pool): block copies (none in this
+workload), the KV write of the 256 new tokens, and decode attention (split-K
+partition pass + merge).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0, N = 1).  The roofline object describes the
+attention call, the dominant cost of the step: algorithmic bytes (every
+valid token's K and V once, plus q, out, tables and lengths) divided by its
+average duration from HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes the decode step must move: K and V of every valid token of every
+    kv head, the query rows read, the fp32 outputs written, the block-table
+    entries in use and the lengths."""
+    L = w.seq_lens.astype(np.int64)
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * w.dtype_bytes
+    q = w.batch * w.num_q_heads * w.head_size * w.dtype_bytes
+    out = w.batch * w.num_q_heads * w.head_size * 4
+    tables = int(((L + 15) // 16).sum()) * 4
+    return kv + q + out + tables + 4 * w.batch
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The oracle (unchanged) on the host: textbook fp64 attention of whole
+    decode rows, one sequence at a time, single-threaded BLAS."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import scenario
+    order = np.random.default_rng(1).permutation(w.batch)
+    done_rows = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1):
+        for s in order:
+            scenario.sequence_attention(w, int(s))
+            done_rows += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done_rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_rows} of {w.batch} decode rows of the same workload "
+                      f"(all {w.num_q_heads} heads each), fp64 NumPy, 1 thread, {dt:.1f} s"}
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mb", type=int, default=0,
+                    help="write this many MiB of scratch between timed steps (0 = back to back)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from paged_kv_attention_06_amd import step as gpu_step
+
+    lib = os.path.join(ROOT, "paged_kv_attention_06_amd", "libpkv.so")
+    if not os.path.exists(lib):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    w = workloads.make(3)
+    st = gpu_step.PagedStep(w, "cuda")
+    st.build_history()
+    st.prepare_step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device="cuda")
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if args.flush_mb:
+            flush.fill_(i & 0xFF)
+        a, b, c = ev[i]
+        a.record(stream)
+        st.copy_and_write()
+        b.record(stream)
+        st.attend()
+        c.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
+    attn_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_per_step = float(step_ms.mean())
+    attn_mean = float(attn_ms.mean())
+    alg = algorithmic_bytes(w)
+    achieved = alg / (attn_mean * 1e-3) / 1e9
+    value = w.batch / (ms_per_step * 1e-3)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B-shaped GQA decode: 32 q / 8 kv heads, head 128, bf16 "
+                        "N(0,1), batch 256, lognormal contexts (median 800, sigma 1, "
+                        "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool",
+            "global_batch": w.batch,
+            "sum_context_tokens": int(w.seq_lens.sum()),
+            "parallelism": "none (1 GPU)",
+            "flush_mb_between_steps": args.flush_mb,
+        },
+        "attention_ms": attn_mean,
+        "attention_ms_p10_p90": [float(np.percentile(attn_ms, 10)), float(np.percentile(attn_ms, 90))],
+        "write_ms": float((step_ms - attn_ms).mean()),
+        "hbm_gbps": achieved,
+        "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "wall_s_timed_region": wall,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": None,
+            "kernel": "paged_attention_decode (k_decode_partition + k_decode_merge)",
+            "algorithmic_bytes_per_launch": alg,
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * pkv.h -- paged KV-cache attention for AMD MI355X (gfx950), C ABI.
+ *
+ * PagedAttention keeps every sequence's keys and values in fixed blocks of
+ * 16 tokens that may sit anywhere in a pool; a per-sequence block table maps
+ * logical block i to a physical block id, like an OS page table, and the
+ * attention kernel walks that table (vLLM 技术内幕 (openeuler), section 2.1;
+ * Continuous batching + PagedAttention (juhe.plus), sections 3.2, 3.3, 3.6).
+ * New tokens' K/V are scattered to the slots named by a slot_mapping
+ * (vLLM 源码精读, section 5.1).
+ *
+ * Conventions for every entry point
+ *  - Pointers documented "device" must point to GPU memory of the current
+ *    device; "host" pointers to ordinary CPU memory.  The caller owns every
+ *    buffer; the library allocates no device memory and keeps no state
+ *    between calls except pkv_pool objects the caller creates and destroys.
+ *  - GPU work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream), asynchronously to the host.  No entry point synchronises or
+ *    reads device memory from the host.
+ *  - Return value: PKV_OK (0) or a PKV_ERR_* code.  Arguments are checked on
+ *    the host before anything is launched; on an error nothing is launched
+ *    and pkv_last_error() describes it.  Contents of device buffers (slots,
+ *    table entries, lengths) cannot be checked without a copy; they are the
+ *    caller's preconditions, stated per call.
+ *
+ * KV pool layout (bytes; es = element size, E = 16 / es elements per
+ * 16-byte granule, bs = block_size = 16, D = head_size):
+ *    pool[num_blocks][num_kv_heads][2][bs * D * es]
+ *  index 0 of the "2" is the K tile, 1 the V tile of one (block, kv head):
+ *    K tile: element (t, d) at element offset ((d / E) * bs + t) * E + d % E
+ *            (16-byte granules of E consecutive d of one token, granule-major)
+ *    V tile: element (t, d) at element offset ((t / E) * D + d) * E + t % E
+ *            (16-byte granules of E consecutive tokens of one d)
+ *  A block therefore holds 2 * bs * num_kv_heads * D * es bytes, the
+ *  per-block figure of Inside vLLM ("Engine construction"), and every
+ *  (block, kv head) K or V tile is one contiguous run.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = 1,      /* a required pointer is NULL                      */
+  PKV_ERR_DIM = 2,       /* unsupported or inconsistent size / count        */
+  PKV_ERR_DTYPE = 3,     /* unsupported element type                        */
+  PKV_ERR_WORKSPACE = 4, /* workspace smaller than required                 */
+  PKV_ERR_HIP = 5,       /* a HIP launch failed (text in pkv_last_error)    */
+  PKV_ERR_NOMEM = 6,     /* pkv_pool has too few free blocks                */
+  PKV_ERR_RANGE = 7      /* a host-visible index or length is out of range  */
+};
+
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Static text for a status code. */
+const char* pkv_status_string(int status);
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+/* ------------------------------------------------------------ the cache */
+typedef struct pkv_cache {
+  void* kv;             /* device: the pool, layout above                    */
+  int64_t num_blocks;   /* blocks in the pool, >= 1                          */
+  int32_t block_size;   /* tokens per block; must be 16                      */
+  int32_t num_kv_heads; /* >= 1                                              */
+  int32_t head_size;    /* 64 or 128                                         */
+  int32_t dtype;        /* PKV_F32 or PKV_BF16                               */
+} pkv_cache;
+
+/* Bytes of one block over all kv heads, K and V:
+ * 2 * block_size * num_kv_heads * head_size * dtype_bytes
+ * (Inside vLLM, "Engine construction").  0 if the descriptor is invalid;
+ * cache->kv may be NULL here. */
+size_t pkv_block_bytes(const pkv_cache* cache);
+
+/* ------------------------------------------------------ host metadata */
+/* Slot of every new token of a step (vLLM 源码精读, section 5.1;
+ * juhe.plus section 3.3): sequence s owns rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1; row i sits at position
+ * p = seq_lens[s] - q_len_s + i and goes to slot
+ * block_tables[s][p / block_size] * block_size + p % block_size.
+ *   block_tables    host int32 [num_seqs][max_blocks_per_seq], row-major
+ *   query_start_loc host int32 [num_seqs + 1], non-decreasing, from 0
+ *   seq_lens        host int32 [num_seqs], q_len_s <= seq_lens[s] <=
+ *                   max_blocks_per_seq * block_size
+ *   slot_mapping    host int64 [query_start_loc[num_seqs]] (output)
+ * Errors: PKV_ERR_NULL, PKV_ERR_DIM (block_size != 16, counts < 0),
+ * PKV_ERR_RANGE (a length outside the bounds above or a negative table
+ * entry on the path). */
+int pkv_build_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* query_start_loc, const int32_t* seq_lens,
+                           int32_t num_seqs, int32_t block_size, int64_t* slot_mapping);
+
+/* ---------------------------------------------------- KV write (scatter) */
+/* Write each new token's K and V rows, all kv heads, into its slot
+ * (vLLM 技术内幕 section 2.1: write_to_paged_cache / reshape_and_cache).
+ *   k_new, v_new  device [num_tokens][num_kv_heads][head_size], contiguous,
+ *                 same element type as the cache (bits are copied as is)
+ *   slot_mapping  device int64 [num_tokens]; slot < 0 skips the token.
+ * Preconditions on device data: non-negative slots are distinct and
+ * < num_blocks * 16.  num_tokens == 0 is a no-op. */
+int paged_kv_write(const pkv_cache* cache, const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int64_t num_tokens, void* stream);
+
+/* ------------------------------------------------------- block copy (COW) */
+/* For each pair (src, dst) make block dst a copy of block src, K and V of
+ * all kv heads: the copy step of copy-on-write (vLLM 技术内幕 section 2.2;
+ * juhe.plus section 3.8).
+ *   pairs  device int64 [num_pairs][2] = (src, dst)
+ * Preconditions on device data: ids in [0, num_blocks); dsts distinct; no
+ * dst is also a src (so every read sees the pre-call contents; a src may
+ * repeat).  num_pairs == 0 is a no-op. */
+int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, void* stream);
+
+/* ------------------------------------------------------------ attention */
+/* Workspace bytes paged_attention_decode / paged_attention_mixed need for
+ * these host lengths (split-K partials).  h_query_start_loc may be NULL for
+ * a pure decode batch (one query row per sequence); cache->kv may be NULL.
+ * 0 on invalid input, and also when no workspace is needed. */
+size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads,
+                                     const int32_t* h_query_start_loc,
+                                     const int32_t* h_seq_lens, int32_t num_seqs);
+
+/* Decode attention: one query row per sequence attends to all seq_lens[s]
+ * keys of its sequence through its block table (juhe.plus section 3.6;
+ * vLLM 技术内幕 section 2.1).  Query head h reads kv head
+ * h / (num_q_heads / num_kv_heads).
+ *   out           device float32 [num_seqs][num_q_heads][head_size]
+ *   q             device [num_seqs][num_q_heads][head_size], cache dtype
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]
+ *   h_seq_lens    host copy of seq_lens (sizes the grid; must be equal)
+ *   scale         multiplies q.k before the softmax (usually 1/sqrt(D))
+ *   workspace     device, >= pkv_attention_workspace_bytes(...) bytes
+ * A sequence of length 0 yields a zero row.  Preconditions on device data:
+ * the first ceil(seq_lens[s]/16) table entries of row s are valid block
+ * ids; the K/V of every position < seq_lens[s] were written. */
+int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
+                           int32_t num_q_heads, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* h_seq_lens, int32_t num_seqs, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Mixed step: chunked-prefill rows and decode rows in one flattened batch
+ * (Inside vLLM, "Forward pass" and "Chunked prefill"; juhe.plus section
+ * 4.2).  Sequence s owns query rows query_start_loc[s] ..
+ * query_start_loc[s+1]-1; row i sits at position seq_lens[s] - q_len_s + i
+ * and sees keys 0..that position (causal).  The step's own K/V must already
+ * be written (paged_kv_write on the same stream).
+ *   out    device float32 [num_tokens][num_q_heads][head_size]
+ *   q      device [num_tokens][num_q_heads][head_size], cache dtype
+ *   query_start_loc, seq_lens: device int32; h_*: equal host copies
+ *   num_tokens == query_start_loc[num_seqs]
+ * Host-checked: q_len_s <= seq_lens[s] <= max_blocks_per_seq * 16. */
+int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
+                          int32_t num_q_heads, const int32_t* query_start_loc,
+                          const int32_t* seq_lens, const int32_t* h_query_start_loc,
+                          const int32_t* h_seq_lens, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, int32_t num_seqs, int64_t num_tokens,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------- host block allocator */
+/* A pool of block ids with reference counts (vLLM 技术内幕 section 2.1-2.2;
+ * Inside vLLM "Scheduler": allocate_slots pops the first n free blocks).
+ * Host only; the caller applies the returned copy pairs with block_copy and
+ * the returned slots with paged_kv_write. */
+typedef struct pkv_pool pkv_pool;
+
+/* free_order (host int32 [num_blocks], a permutation of 0..num_blocks-1,
+ * or NULL for ascending) is the order blocks are handed out.  NULL on
+ * invalid input or out of host memory. */
+pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t block_size);
+void pkv_pool_destroy(pkv_pool* pool);
+int64_t pkv_pool_num_free(const pkv_pool* pool);
+/* Reference count of a block, -1 if the id is out of range. */
+int32_t pkv_pool_refcnt(const pkv_pool* pool, int32_t block_id);
+
+/* Make room for n_new tokens after cur_len cached ones of a sequence whose
+ * table (host int32, capacity max_blocks) holds ceil(cur_len/16) ids.
+ * If the last block is partly filled and shared (ref > 1) it is first
+ * replaced by a fresh block: cow_pair = (old, new), the old block loses one
+ * reference (copy-on-write, juhe.plus section 3.8); otherwise cow_pair =
+ * (-1, -1).  Then ceil((cur_len+n_new)/16) - ceil(cur_len/16) blocks are
+ * appended.  slots (host int64 [n_new]) receives the new tokens' slots.
+ * On PKV_ERR_NOMEM / PKV_ERR_RANGE nothing changes. */
+int pkv_pool_append(pkv_pool* pool, int32_t* table, int32_t max_blocks, int32_t cur_len,
+                    int32_t n_new, int64_t* slots, int64_t* cow_pair);
+
+/* Share a sequence's blocks with a new holder (parallel sampling,
+ * juhe.plus section 3.5): every id gains one reference and is copied to
+ * out_table (host int32 [num_table_blocks]). */
+int pkv_pool_fork(pkv_pool* pool, const int32_t* table, int32_t num_table_blocks,
+                  int32_t* out_table);
+
+/* Drop one reference of each listed block, last first; a block whose count
+ * reaches 0 goes to the head of the free list (reused first). */
+int pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t num_table_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKV_H */

@@ -1,0 +1,25 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950).
+
+The compute path is libpkv.so (hand-written HIP kernels behind a C ABI,
+include/pkv.h); this package is its ctypes binding.  Importing it fails
+loudly when the library has not been built.
+"""
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    PKV_BF16,
+    PKV_F32,
+    Cache,
+    PkvCache,
+    PkvError,
+    Pool,
+    block_copy,
+    descriptor,
+    paged_attention_decode,
+    paged_attention_mixed,
+    paged_kv_write,
+    pkv_attention_workspace_bytes,
+    pkv_block_bytes,
+    pkv_build_slot_mapping,
+    status_string,
+    version,
+)

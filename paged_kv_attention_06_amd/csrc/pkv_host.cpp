@@ -1,0 +1,393 @@
+// Host side of the C ABI declared in include/pkv.h: argument checks, work
+// sizing, launches, the slot-mapping builder and the block allocator.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PKV_OK;
+}
+
+int dtype_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+  }
+  return 0;
+}
+
+// Checks the descriptor; fills `d` on success.  Sizing queries pass
+// need_kv = false and accept a NULL pool pointer.
+int check_cache(const pkv_cache* c, pkv::CacheDesc* d, bool need_kv = true) {
+  if (!c) return fail(PKV_ERR_NULL, "cache descriptor is NULL");
+  if (need_kv && !c->kv) return fail(PKV_ERR_NULL, "cache->kv is NULL");
+  if (c->block_size != pkv::kBlockSize)
+    return fail(PKV_ERR_DIM, "block_size %d unsupported (must be 16)", c->block_size);
+  if (c->num_blocks < 1) return fail(PKV_ERR_DIM, "num_blocks %lld < 1", (long long)c->num_blocks);
+  if (c->num_kv_heads < 1) return fail(PKV_ERR_DIM, "num_kv_heads %d < 1", c->num_kv_heads);
+  if (c->head_size != 64 && c->head_size != 128)
+    return fail(PKV_ERR_DIM, "head_size %d unsupported (64 or 128)", c->head_size);
+  const int es = dtype_bytes(c->dtype);
+  if (!es) return fail(PKV_ERR_DTYPE, "dtype %d unsupported", c->dtype);
+  d->kv = static_cast<char*>(c->kv);
+  d->num_blocks = c->num_blocks;
+  d->hkv = c->num_kv_heads;
+  d->head_size = c->head_size;
+  d->dtype_bytes = es;
+  d->block_bytes = (size_t)2 * c->block_size * c->num_kv_heads * c->head_size * es;
+  return PKV_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+struct Plan {
+  int64_t decode_units = 0;
+  int64_t prefill_tiles = 0;
+  int prefill_seqs = 0;
+  int64_t num_tokens = 0;
+};
+
+// Validates host lengths and counts the work.  qsl may be NULL (decode).
+int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs,
+                   int32_t max_blocks, Plan* plan) {
+  if (!seq_lens) return fail(PKV_ERR_NULL, "host seq_lens is NULL");
+  if (num_seqs < 0) return fail(PKV_ERR_DIM, "num_seqs %d < 0", num_seqs);
+  if (max_blocks < 0) return fail(PKV_ERR_DIM, "max_blocks_per_seq %d < 0", max_blocks);
+  if (qsl && qsl[0] != 0) return fail(PKV_ERR_RANGE, "query_start_loc[0] = %d, must be 0", qsl[0]);
+  const int64_t cap = (int64_t)max_blocks * pkv::kBlockSize;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t L = seq_lens[s];
+    const int64_t ql = qsl ? (int64_t)qsl[s + 1] - qsl[s] : 1;
+    if (ql < 0) return fail(PKV_ERR_RANGE, "query_start_loc decreases at sequence %d", s);
+    if (L < 0 || L > cap)
+      return fail(PKV_ERR_RANGE, "seq_lens[%d] = %lld outside [0, %lld]", s, (long long)L,
+                  (long long)cap);
+    if (qsl && ql > L)
+      return fail(PKV_ERR_RANGE, "sequence %d has %lld query rows but length %lld", s,
+                  (long long)ql, (long long)L);
+    if (ql == 1) {
+      if (L > 0) plan->decode_units += (L + pkv::kPartTokens - 1) / pkv::kPartTokens;
+    } else if (ql > 1) {
+      plan->prefill_tiles += (ql + pkv::kPrefillTileQ - 1) / pkv::kPrefillTileQ;
+      plan->prefill_seqs += 1;
+    }
+    plan->num_tokens += ql;
+  }
+  return PKV_OK;
+}
+
+size_t workspace_for(const Plan& p, int hq, int D) {
+  return (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+}
+
+int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,
+              const int32_t* qsl, const int32_t* seq_lens, const int32_t* h_qsl,
+              const int32_t* h_seq_lens, const int32_t* block_tables, int32_t max_blocks,
+              int32_t num_seqs, int64_t num_tokens, float scale, void* workspace,
+              size_t ws_bytes, void* stream, bool mixed) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c)) return e;
+  if (num_q_heads < 1 || num_q_heads % c.hkv != 0)
+    return fail(PKV_ERR_DIM, "num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                num_q_heads, c.hkv);
+  if (!pkv::supported_group(num_q_heads / c.hkv))
+    return fail(PKV_ERR_DIM, "%d query heads per kv head unsupported (1, 2, 4 or 8)",
+                num_q_heads / c.hkv);
+  if (mixed && !h_qsl) return fail(PKV_ERR_NULL, "host query_start_loc is NULL");
+  Plan plan;
+  if (int e = plan_attention(mixed ? h_qsl : nullptr, h_seq_lens, num_seqs, max_blocks, &plan))
+    return e;
+  if (mixed && plan.num_tokens != num_tokens)
+    return fail(PKV_ERR_RANGE, "query_start_loc[num_seqs] = %lld but num_tokens = %lld",
+                (long long)plan.num_tokens, (long long)num_tokens);
+  if (plan.num_tokens == 0 && num_seqs == 0) return ok();
+  if (!out || !q || !seq_lens || !block_tables || (mixed && !qsl))
+    return fail(PKV_ERR_NULL, "a device pointer (out, q, seq_lens, block_tables%s) is NULL",
+                mixed ? ", query_start_loc" : "");
+  const size_t need = workspace_for(plan, num_q_heads, c.head_size);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+  pkv::AttnDesc a;
+  a.out = out;
+  a.q = q;
+  a.hq = num_q_heads;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.seq_lens = seq_lens;
+  a.query_start_loc = mixed ? qsl : nullptr;
+  a.num_seqs = num_seqs;
+  a.scale = scale;
+  a.ws_acc = static_cast<float*>(workspace);
+  a.ws_ml = a.ws_acc ? a.ws_acc + (size_t)plan.decode_units * num_q_heads * c.head_size : nullptr;
+  a.decode_units = plan.decode_units;
+  a.prefill_tiles = plan.prefill_tiles;
+  a.prefill_seqs = plan.prefill_seqs;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.prefill_tiles > 0) {
+    if (int e = hip_status(pkv::launch_prefill_rows(c, a, st), "prefill rows")) return e;
+  }
+  return hip_status(pkv::launch_decode_rows(c, a, st), "decode rows");
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "null pointer";
+    case PKV_ERR_DIM: return "unsupported or inconsistent dimension";
+    case PKV_ERR_DTYPE: return "unsupported dtype";
+    case PKV_ERR_WORKSPACE: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP error";
+    case PKV_ERR_NOMEM: return "no free blocks";
+    case PKV_ERR_RANGE: return "index or length out of range";
+  }
+  return "unknown status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_version(void) { return 100; }
+
+size_t pkv_block_bytes(const pkv_cache* cache) {
+  pkv::CacheDesc c;
+  if (check_cache(cache, &c, false)) return 0;
+  return c.block_bytes;
+}
+
+int pkv_build_slot_mapping(const int32_t* block_tables, int32_t max_blocks,
+                           const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t block_size, int64_t* slots) {
+  if (block_size != pkv::kBlockSize)
+    return fail(PKV_ERR_DIM, "block_size %d unsupported (must be 16)", block_size);
+  if (num_seqs < 0 || max_blocks < 0) return fail(PKV_ERR_DIM, "negative count");
+  if (num_seqs == 0) return ok();
+  if (!block_tables || !qsl || !seq_lens || !slots)
+    return fail(PKV_ERR_NULL, "a host pointer is NULL");
+  if (qsl[0] != 0) return fail(PKV_ERR_RANGE, "query_start_loc[0] = %d, must be 0", qsl[0]);
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t q_len = (int64_t)qsl[s + 1] - qsl[s];
+    const int64_t L = seq_lens[s];
+    if (q_len < 0 || L < q_len || L > cap)
+      return fail(PKV_ERR_RANGE, "sequence %d: q_len %lld, length %lld, capacity %lld", s,
+                  (long long)q_len, (long long)L, (long long)cap);
+    const int32_t* row = block_tables + (int64_t)s * max_blocks;
+    for (int64_t i = 0; i < q_len; ++i) {
+      const int64_t pos = L - q_len + i;
+      const int32_t phys = row[pos / block_size];
+      if (phys < 0)
+        return fail(PKV_ERR_RANGE, "sequence %d: table entry %lld is negative", s,
+                    (long long)(pos / block_size));
+      slots[qsl[s] + i] = (int64_t)phys * block_size + pos % block_size;
+    }
+  }
+  return ok();
+}
+
+int paged_kv_write(const pkv_cache* cache, const void* k_new, const void* v_new,
+                   const int64_t* slot_mapping, int64_t num_tokens, void* stream) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c)) return e;
+  if (num_tokens < 0) return fail(PKV_ERR_DIM, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens == 0) return ok();
+  if (!k_new || !v_new || !slot_mapping) return fail(PKV_ERR_NULL, "k_new, v_new or slot_mapping is NULL");
+  return hip_status(pkv::launch_kv_write(c, k_new, v_new, slot_mapping, num_tokens,
+                                         static_cast<hipStream_t>(stream)),
+                    "paged_kv_write");
+}
+
+int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, void* stream) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c)) return e;
+  if (num_pairs < 0) return fail(PKV_ERR_DIM, "num_pairs %lld < 0", (long long)num_pairs);
+  if (num_pairs == 0) return ok();
+  if (!pairs) return fail(PKV_ERR_NULL, "pairs is NULL");
+  return hip_status(pkv::launch_block_copy(c, pairs, num_pairs, static_cast<hipStream_t>(stream)),
+                    "block_copy");
+}
+
+size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads,
+                                     const int32_t* h_qsl, const int32_t* h_seq_lens,
+                                     int32_t num_seqs) {
+  pkv::CacheDesc c;
+  if (check_cache(cache, &c, false) || num_q_heads < 1) return 0;
+  Plan plan;
+  if (plan_attention(h_qsl, h_seq_lens, num_seqs, INT32_MAX / pkv::kBlockSize, &plan)) return 0;
+  return workspace_for(plan, num_q_heads, c.head_size);
+}
+
+int paged_attention_decode(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, const int32_t* h_seq_lens, int32_t num_seqs,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention(cache, out, q, num_q_heads, nullptr, seq_lens, nullptr, h_seq_lens,
+                   block_tables, max_blocks_per_seq, num_seqs, num_seqs, scale, workspace,
+                   workspace_bytes, stream, false);
+}
+
+int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,
+                          const int32_t* query_start_loc, const int32_t* seq_lens,
+                          const int32_t* h_query_start_loc, const int32_t* h_seq_lens,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          int32_t num_seqs, int64_t num_tokens, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return attention(cache, out, q, num_q_heads, query_start_loc, seq_lens, h_query_start_loc,
+                   h_seq_lens, block_tables, max_blocks_per_seq, num_seqs, num_tokens, scale,
+                   workspace, workspace_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// host block allocator
+// ---------------------------------------------------------------------------
+struct pkv_pool {
+  int32_t block_size;
+  std::vector<int32_t> ref;
+  std::deque<int32_t> free_list;
+};
+
+pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t block_size) {
+  if (num_blocks < 1 || num_blocks > INT32_MAX || block_size != pkv::kBlockSize) {
+    fail(PKV_ERR_DIM, "pkv_pool_create: num_blocks %lld, block_size %d", (long long)num_blocks,
+         block_size);
+    return nullptr;
+  }
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return nullptr;
+  p->block_size = block_size;
+  p->ref.assign((size_t)num_blocks, 0);
+  std::vector<char> seen;
+  if (free_order) seen.assign((size_t)num_blocks, 0);
+  for (int64_t i = 0; i < num_blocks; ++i) {
+    const int32_t b = free_order ? free_order[i] : (int32_t)i;
+    if (free_order) {
+      if (b < 0 || b >= num_blocks || seen[(size_t)b]) {
+        fail(PKV_ERR_RANGE, "pkv_pool_create: free_order is not a permutation (entry %lld = %d)",
+             (long long)i, b);
+        delete p;
+        return nullptr;
+      }
+      seen[(size_t)b] = 1;
+    }
+    p->free_list.push_back(b);
+  }
+  ok();
+  return p;
+}
+
+void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
+
+int64_t pkv_pool_num_free(const pkv_pool* pool) {
+  return pool ? (int64_t)pool->free_list.size() : -1;
+}
+
+int32_t pkv_pool_refcnt(const pkv_pool* pool, int32_t block_id) {
+  if (!pool || block_id < 0 || (size_t)block_id >= pool->ref.size()) return -1;
+  return pool->ref[(size_t)block_id];
+}
+
+int pkv_pool_append(pkv_pool* pool, int32_t* table, int32_t max_blocks, int32_t cur_len,
+                    int32_t n_new, int64_t* slots, int64_t* cow_pair) {
+  if (!pool || !cow_pair || (!table && max_blocks > 0) || (!slots && n_new > 0))
+    return fail(PKV_ERR_NULL, "pkv_pool_append: NULL argument");
+  if (cur_len < 0 || n_new < 0 || max_blocks < 0)
+    return fail(PKV_ERR_DIM, "pkv_pool_append: negative count");
+  const int64_t bs = pool->block_size;
+  const int64_t have = (cur_len + bs - 1) / bs;
+  const int64_t need = ((int64_t)cur_len + n_new + bs - 1) / bs;
+  if (need > max_blocks)
+    return fail(PKV_ERR_RANGE, "pkv_pool_append: %lld blocks exceed table capacity %d",
+                (long long)need, max_blocks);
+  for (int64_t i = 0; i < have; ++i) {
+    if (table[i] < 0 || (size_t)table[i] >= pool->ref.size() || pool->ref[(size_t)table[i]] < 1)
+      return fail(PKV_ERR_RANGE, "pkv_pool_append: table entry %lld (%d) is not a held block",
+                  (long long)i, table[i]);
+  }
+  const bool into_partial = n_new > 0 && (cur_len % bs) != 0;
+  const bool copy = into_partial && pool->ref[(size_t)table[have - 1]] > 1;
+  const int64_t fresh = (need - have) + (copy ? 1 : 0);
+  if (fresh > (int64_t)pool->free_list.size())
+    return fail(PKV_ERR_NOMEM, "pkv_pool_append: %lld blocks needed, %zu free", (long long)fresh,
+                pool->free_list.size());
+  cow_pair[0] = cow_pair[1] = -1;
+  auto take = [pool]() {
+    const int32_t b = pool->free_list.front();
+    pool->free_list.pop_front();
+    pool->ref[(size_t)b] = 1;
+    return b;
+  };
+  if (copy) {
+    const int32_t old_b = table[have - 1];
+    const int32_t new_b = take();
+    pool->ref[(size_t)old_b] -= 1;
+    table[have - 1] = new_b;
+    cow_pair[0] = old_b;
+    cow_pair[1] = new_b;
+  }
+  for (int64_t i = have; i < need; ++i) table[i] = take();
+  for (int64_t i = 0; i < n_new; ++i) {
+    const int64_t pos = (int64_t)cur_len + i;
+    slots[i] = (int64_t)table[pos / bs] * bs + pos % bs;
+  }
+  return ok();
+}
+
+int pkv_pool_fork(pkv_pool* pool, const int32_t* table, int32_t n, int32_t* out_table) {
+  if (!pool || (n > 0 && (!table || !out_table))) return fail(PKV_ERR_NULL, "pkv_pool_fork: NULL argument");
+  if (n < 0) return fail(PKV_ERR_DIM, "pkv_pool_fork: negative count");
+  for (int32_t i = 0; i < n; ++i) {
+    if (table[i] < 0 || (size_t)table[i] >= pool->ref.size() || pool->ref[(size_t)table[i]] < 1)
+      return fail(PKV_ERR_RANGE, "pkv_pool_fork: entry %d (%d) is not a held block", i, table[i]);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    pool->ref[(size_t)table[i]] += 1;
+    out_table[i] = table[i];
+  }
+  return ok();
+}
+
+int pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t n) {
+  if (!pool || (n > 0 && !table)) return fail(PKV_ERR_NULL, "pkv_pool_release: NULL argument");
+  if (n < 0) return fail(PKV_ERR_DIM, "pkv_pool_release: negative count");
+  for (int32_t i = 0; i < n; ++i) {
+    if (table[i] < 0 || (size_t)table[i] >= pool->ref.size() || pool->ref[(size_t)table[i]] < 1)
+      return fail(PKV_ERR_RANGE, "pkv_pool_release: entry %d (%d) is not a held block", i, table[i]);
+  }
+  for (int32_t i = n - 1; i >= 0; --i) {
+    int32_t& r = pool->ref[(size_t)table[i]];
+    r -= 1;
+    if (r == 0) pool->free_list.push_front(table[i]);
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI host layer (pkv_host.cpp) and the
+// HIP kernels (pkv_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;
+// Split-K partition length of the decode kernel, in tokens (a multiple of
+// the 64 tokens one wave covers per step).  The workspace size depends on it.
+constexpr int kPartTokens = 256;
+// Query positions per prefill tile (each tile also packs every query head of
+// one kv-head group into its rows).
+constexpr int kPrefillTileQ = 16;
+
+struct CacheDesc {
+  char* kv;
+  int64_t num_blocks;
+  int hkv;
+  int head_size;
+  int dtype_bytes;
+  size_t block_bytes;  // 2 * 16 * hkv * D * es
+};
+
+struct AttnDesc {
+  float* out;
+  const void* q;
+  int hq;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;  // nullptr: pure decode, row s = sequence s
+  int num_seqs;
+  float scale;
+  float* ws_acc;                   // [units][hq][D]
+  float* ws_ml;                    // [units][hq][2]
+  int64_t decode_units;            // split-K work units over all decode rows
+  int64_t prefill_tiles;           // prefill q-tiles over all prefill rows
+  int prefill_seqs;                // sequences with more than one query row
+};
+
+hipError_t launch_kv_write(const CacheDesc& c, const void* k_new, const void* v_new,
+                           const int64_t* slots, int64_t num_tokens, hipStream_t stream);
+hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t num_pairs,
+                             hipStream_t stream);
+// Decode rows (one query row per sequence, or the q_len == 1 rows of a mixed
+// batch): split-K partition pass, then the merge of multi-partition rows.
+hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
+// Prefill rows of a mixed batch (q_len > 1): MFMA tiles.
+hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
+
+bool supported_group(int g);
+
+}  // namespace pkv

@@ -1,0 +1,560 @@
+// HIP kernels of the paged KV-cache path for gfx950 (CDNA4, wave64).
+//
+//  * kv write      : scatter of new tokens' K/V granules to their slots
+//                    (vLLM 技术内幕, section 2.1: reshape_and_cache).
+//  * block copy    : copy-on-write data move (juhe.plus, section 3.8).
+//  * decode        : split-K over 256-token partitions of each sequence;
+//                    each wave walks its partition's blocks through the
+//                    block table (juhe.plus, section 3.6), keeps an online
+//                    softmax and writes either the final row or a partial
+//                    (max, sum, weighted V) that a merge pass combines.
+//
+// Pool layout (see pkv.h): pool[block][kv_head][K|V][tile]; a K tile is
+// 16-byte granules of E consecutive d of one token, granule-major; a V tile
+// is 16-byte granules of E consecutive tokens of one d.  With that layout a
+// wave reads a K tile with lane = token (16 lanes x 16 B contiguous per
+// granule) and a V tile with lane = d (64 lanes x 16 B contiguous), both as
+// whole 16-byte loads, so no transpose through LDS is needed.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int BS = kBlockSize;
+constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescale: the running max is only raised when a new score exceeds it
+// by more than this (log2 units), so probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int ES>
+__device__ __forceinline__ float granule_elem(const uint4& g, int e) {
+  const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+  if constexpr (ES == 4) {
+    return __uint_as_float(w[e]);
+  } else {
+    return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Max / sum over the 64 lanes of the wave; every lane gets the same value.
+// Rows of 16 lanes are reduced with DPP (quad swaps, half-row and row
+// mirrors), then the four row results are combined.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ---------------------------------------------------------------------------
+// KV write: one thread per (token, kv head, 16-byte granule of the row).
+// ---------------------------------------------------------------------------
+template <int ES>
+__global__ __launch_bounds__(256) void k_kv_write(char* __restrict__ kv, size_t block_bytes,
+                                                  int hkv, int D, const uint4* __restrict__ k_new,
+                                                  const uint4* __restrict__ v_new,
+                                                  const int64_t* __restrict__ slots, int64_t total) {
+  constexpr int E = 16 / ES;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int KG = D / E;
+  const int c = (int)(i % KG);
+  const int64_t r = i / KG;
+  const int h = (int)(r % hkv);
+  const int64_t t = r / hkv;
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  char* head = kv + blk * (int64_t)block_bytes + (int64_t)h * (2 * BS * D * ES);
+  // K: the granule keeps its 16 bytes; it moves to granule index c * BS + off.
+  *reinterpret_cast<uint4*>(head + (c * BS + off) * 16) = k_new[i];
+  // V: element d = c * E + e of token off goes to ((off / E) * D + d) * E + off % E.
+  const uint4 g = v_new[i];
+  char* vt = head + BS * D * ES;
+  const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = c * E + e;
+    const int64_t el = ((int64_t)(off / E) * D + d) * E + (off % E);
+    if constexpr (ES == 4) {
+      reinterpret_cast<uint32_t*>(vt)[el] = w[e];
+    } else {
+      reinterpret_cast<uint16_t*>(vt)[el] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+    }
+  }
+}
+
+hipError_t launch_kv_write(const CacheDesc& c, const void* k_new, const void* v_new,
+                           const int64_t* slots, int64_t num_tokens, hipStream_t stream) {
+  const int64_t total = num_tokens * c.hkv * (c.head_size * c.dtype_bytes / 16);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (c.dtype_bytes == 4)
+    hipLaunchKernelGGL(k_kv_write<4>, grid, dim3(256), 0, stream, c.kv, c.block_bytes, c.hkv,
+                       c.head_size, (const uint4*)k_new, (const uint4*)v_new, slots, total);
+  else
+    hipLaunchKernelGGL(k_kv_write<2>, grid, dim3(256), 0, stream, c.kv, c.block_bytes, c.hkv,
+                       c.head_size, (const uint4*)k_new, (const uint4*)v_new, slots, total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block copy: one thread per 16-byte granule of each (src, dst) pair.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_block_copy(char* __restrict__ kv, int64_t granules_per_block,
+                                                    const int64_t* __restrict__ pairs, int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t pr = i / granules_per_block;
+  const int64_t g = i % granules_per_block;
+  const int64_t src = pairs[2 * pr];
+  const int64_t dst = pairs[2 * pr + 1];
+  const uint4* s = reinterpret_cast<const uint4*>(kv) + src * granules_per_block + g;
+  uint4* d = reinterpret_cast<uint4*>(kv) + dst * granules_per_block + g;
+  *d = *s;
+}
+
+hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t num_pairs,
+                             hipStream_t stream) {
+  const int64_t gpb = (int64_t)(c.block_bytes / 16);
+  const int64_t total = gpb * num_pairs;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_copy, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     c.kv, gpb, pairs, total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode work units.  A unit is one 256-token partition of one decode row;
+// units are numbered sequence by sequence.  A wave finds its unit's sequence
+// with a scan over the lengths (cheap next to the 128 KiB it then reads).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int decode_parts(const int32_t* seq_lens, const int32_t* qsl, int s) {
+  const int L = seq_lens[s];
+  const int ql = qsl ? qsl[s + 1] - qsl[s] : 1;
+  return (ql == 1 && L > 0) ? (L + kPartTokens - 1) / kPartTokens : 0;
+}
+
+// Sum over sequences [0, s_end) of decode_parts; every lane gets it.
+__device__ int parts_before(const int32_t* seq_lens, const int32_t* qsl, int s_end) {
+  const int lane = threadIdx.x & 63;
+  int acc = 0;
+  for (int s0 = 0; s0 < s_end; s0 += 64) {
+    const int s = s0 + lane;
+    int n = (s < s_end) ? decode_parts(seq_lens, qsl, s) : 0;
+    acc += n;
+  }
+  return (int)wave_sum((float)acc);  // exact: counts stay far below 2^24
+}
+
+// Find (sequence, partition, partitions of that sequence) of unit u.
+__device__ bool find_unit(int u, const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
+                          int& s_out, int& part_out, int& nparts_out) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int s0 = 0; s0 < num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    const int n = (s < num_seqs) ? decode_parts(seq_lens, qsl, s) : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int total = __shfl(incl, 63);
+    if (u < base + total) {
+      const unsigned long long m = __ballot(base + incl > u);
+      const int ls = __ffsll((unsigned long long)m) - 1;
+      const int incl_s = __shfl(incl, ls);
+      const int n_s = __shfl(n, ls);
+      s_out = uniform(s0 + ls);
+      part_out = uniform(u - (base + incl_s - n_s));
+      nparts_out = uniform(n_s);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// Decode partition pass.  One wave per (unit, kv head); the wave serves all
+// G query heads that share the kv head, so each K/V byte is read once.
+// A step covers 2 blocks = 32 tokens:
+//   K: lanes 2t and 2t+1 of each 32-lane half hold the two halves of token
+//      t's K row; per-lane partial dot products with q (broadcast from LDS)
+//      are completed by one DPP add with the neighbour lane.
+//   softmax: wave max per head; the running max only moves when exceeded by
+//      kRescaleSlack, and then acc and the sums are rescaled.
+//   V: lane = d (D/64 values per lane); probabilities come from LDS.
+// Loads of step i+1 are issued before step i is computed.
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  const char* kv;
+  size_t block_bytes;
+  int hkv;
+  const void* q;
+  float* out;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int num_seqs;
+  float scale_log2;
+  float* ws_acc;
+  float* ws_ml;
+};
+
+template <int ES, int D, int G, bool CHECK>
+__device__ __forceinline__ void pv_block(const uint4 (&vr)[BS * D * ES / 16 / 64],
+                                         const float* __restrict__ p_lds, int key_base,
+                                         int valid_keys, float (&acc)[G][D / 64]) {
+  constexpr int E = 16 / ES;
+  constexpr int VG = BS * D * ES / 16 / 64;
+#pragma unroll
+  for (int i = 0; i < VG; ++i) {
+    const int kg = (i * 64) / D;         // key granule of this load
+    const int dd = ((i * 64) % D) / 64;  // which of the lane's d values
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int key = kg * E + e;
+      if (CHECK && key >= valid_keys) continue;
+      const float v = granule_elem<ES>(vr[i], e);
+      const float* pp = p_lds + (key_base + key) * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(pp[g], v, acc[g][dd]);
+    }
+  }
+}
+
+template <int ES, int D>
+struct DecodeShape {
+  static constexpr int E = 16 / ES;                // elements per granule
+  static constexpr int KG = D / E;                 // granules per K row
+  static constexpr int KH = KG / 2;                // granules per lane (half row)
+  static constexpr int VG = BS * D * ES / 16 / 64; // V granules per lane per block
+  static constexpr int DPL = D / 64;               // d values per lane
+  static constexpr int TILE = BS * D * ES;         // bytes of one K or V tile
+  static constexpr int QROW = KH * 16 + 16;        // LDS bytes of a padded half q row
+};
+
+template <int ES, int D>
+struct StepRegs {
+  uint4 k[DecodeShape<ES, D>::KH];
+  uint4 v[2][DecodeShape<ES, D>::VG];
+};
+
+template <int ES, int D, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_partition(
+    DecodeParams p) {
+  using S = DecodeShape<ES, D>;
+  static_assert(D % 64 == 0, "head size must be a multiple of 64");
+  static_assert(kPartTokens % 32 == 0 && kPartTokens / BS <= 64, "partition size");
+
+  // q rows of the group, each half row padded by 16 bytes so the two halves
+  // read in one instruction fall in different banks.
+  __shared__ __align__(16) char q_lds[G * 2 * S::QROW];
+  __shared__ __align__(16) float p_lds[32 * G];
+
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.x % p.hkv;
+  const int unit = blockIdx.x / p.hkv;
+  int s, part, nparts;
+  if (!find_unit(unit, p.seq_lens, p.qsl, p.num_seqs, s, part, nparts)) return;
+
+  const int L = p.seq_lens[s];
+  const int row = p.qsl ? p.qsl[s] : s;
+  const int hq = p.hkv * G;
+
+  {
+    constexpr int QGR = G * S::KG;  // 16-byte granules of the group's q rows
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + ((size_t)row * hq + (size_t)kvh * G) * D * ES);
+    for (int i = lane; i < QGR; i += 64) {
+      const int g = i / S::KG, c = i % S::KG;
+      const int half = c / S::KH, cc = c % S::KH;
+      *reinterpret_cast<uint4*>(q_lds + (g * 2 + half) * S::QROW + cc * 16) = src[i];
+    }
+  }
+
+  const int tok0 = part * kPartTokens;
+  const int tok_end = min(L, tok0 + kPartTokens);
+  const int nblk = (tok_end - tok0 + BS - 1) / BS;
+  const int nsteps = (nblk + 1) / 2;
+  // lane i < nblk holds the partition's i-th physical block id; later lanes
+  // repeat the last one so over-reads stay inside valid blocks.
+  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks + tok0 / BS;
+  const int my_id = bt[min(lane, nblk - 1)];
+  const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
+
+  const int half = lane & 1;           // which half of the K row
+  const int t_in_blk = (lane >> 1) & 15;
+  const int bsel = lane >> 5;          // which block of the step
+  const int k_lane_off = (half * S::KH * BS + t_in_blk) * 16;
+
+  auto load = [&](StepRegs<ES, D>& r, int st) {
+    const int b0 = uniform(__builtin_amdgcn_readlane(my_id, 2 * st));
+    const int b1 = uniform(__builtin_amdgcn_readlane(my_id, 2 * st + 1));
+    const char* base0 = head_base + (size_t)b0 * p.block_bytes;
+    const char* base1 = head_base + (size_t)b1 * p.block_bytes;
+    const char* kp = (bsel ? base1 : base0) + k_lane_off;
+#pragma unroll
+    for (int c = 0; c < S::KH; ++c) r.k[c] = *reinterpret_cast<const uint4*>(kp + c * BS * 16);
+#pragma unroll
+    for (int i = 0; i < S::VG; ++i) {
+      r.v[0][i] = *reinterpret_cast<const uint4*>(base0 + S::TILE + i * 1024 + lane * 16);
+      r.v[1][i] = *reinterpret_cast<const uint4*>(base1 + S::TILE + i * 1024 + lane * 16);
+    }
+  };
+
+  float m_run[G], l_lane[G], acc[G][S::DPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_lane[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < S::DPL; ++j) acc[g][j] = 0.f;
+  }
+
+  auto compute = [&](const StepRegs<ES, D>& r, int st) {
+    // ---- scores: q granules are read from LDS one step ahead of use; the
+    // compiler barrier keeps the scheduler from hoisting all of them.
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[g] = 0.f;
+    const char* qh = q_lds + half * S::QROW;
+    uint4 qcur[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qcur[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW);
+#pragma unroll
+    for (int c = 0; c < S::KH; ++c) {
+      uint4 qnext[G];
+      const int cn = c + 1 < S::KH ? c + 1 : c;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        qnext[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + cn * 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 qg = qcur[g];
+        const uint4 kg = r.k[c];
+        if constexpr (ES == 2) {
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.x),
+                                                  __builtin_bit_cast(bf16x2_t, kg.x), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.y),
+                                                  __builtin_bit_cast(bf16x2_t, kg.y), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.z),
+                                                  __builtin_bit_cast(bf16x2_t, kg.z), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.w),
+                                                  __builtin_bit_cast(bf16x2_t, kg.w), sc[g], false);
+        } else {
+          sc[g] = fmaf(__uint_as_float(qg.x), __uint_as_float(kg.x), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.y), __uint_as_float(kg.y), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.z), __uint_as_float(kg.z), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.w), __uint_as_float(kg.w), sc[g]);
+        }
+        qcur[g] = qnext[g];
+      }
+      asm volatile("" ::: "memory");
+    }
+
+    // ---- online softmax (log2 domain); the pair of lanes of a token
+    // completes its dot product with one swap-add.
+    const int tok = tok0 + st * 32 + (lane >> 1);
+    const bool tok_ok = tok < tok_end;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float full = sc[g] + dpp_f<0xB1>(sc[g]);
+      const float x = tok_ok ? full * p.scale_log2 : -INFINITY;
+      const float mi = wave_max(x);
+      if (mi > m_run[g] + kRescaleSlack) {
+        const float corr = __builtin_amdgcn_exp2f(m_run[g] - mi);
+        l_lane[g] *= corr;
+#pragma unroll
+        for (int j = 0; j < S::DPL; ++j) acc[g][j] *= corr;
+        m_run[g] = mi;
+      }
+      const float pr = __builtin_amdgcn_exp2f(x - m_run[g]);
+      if (half == 0) {
+        l_lane[g] += pr;
+        p_lds[(lane >> 1) * G + g] = pr;
+      }
+    }
+    __syncthreads();
+
+    // ---- weighted V
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int valid = tok_end - (tok0 + (2 * st + j) * BS);
+      if (valid >= BS)
+        pv_block<ES, D, G, false>(r.v[j], p_lds, j * BS, BS, acc);
+      else if (valid > 0)
+        pv_block<ES, D, G, true>(r.v[j], p_lds, j * BS, valid, acc);
+      asm volatile("" ::: "memory");
+    }
+    __syncthreads();
+  };
+
+  __syncthreads();  // q rows visible
+  StepRegs<ES, D> ra, rb;
+  load(ra, 0);
+  for (int st = 0; st < nsteps; st += 2) {
+    if (st + 1 < nsteps) load(rb, st + 1);
+    compute(ra, st);
+    if (st + 1 < nsteps) {
+      if (st + 2 < nsteps) load(ra, st + 2);
+      compute(rb, st + 1);
+    }
+  }
+
+  float l_tot[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_lane[g]);
+
+  if (nparts == 1) {
+    float* o = p.out + ((size_t)row * hq + (size_t)kvh * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < S::DPL; ++j) o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g];
+    }
+  } else {
+    const size_t w = (size_t)unit * hq + (size_t)kvh * G;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < S::DPL; ++j) p.ws_acc[(w + g) * D + j * 64 + lane] = acc[g][j];
+      if (lane == 0) {
+        p.ws_ml[(w + g) * 2] = m_run[g];
+        p.ws_ml[(w + g) * 2 + 1] = l_tot[g];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge pass for decode rows split over several partitions:
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// One wave per (sequence, kv head); also writes the zero row of an empty
+// sequence.
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p) {
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x;
+  const int kvh = blockIdx.x % p.hkv;
+  const int s = blockIdx.x / p.hkv;
+  const int ql = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
+  if (ql != 1) return;
+  const int L = p.seq_lens[s];
+  const int row = p.qsl ? p.qsl[s] : s;
+  const int hq = p.hkv * G;
+  float* o = p.out + ((size_t)row * hq + (size_t)kvh * G) * D;
+  if (L <= 0) {
+    for (int i = lane; i < G * D; i += 64) o[i] = 0.f;
+    return;
+  }
+  const int nparts = (L + kPartTokens - 1) / kPartTokens;
+  if (nparts == 1) return;
+  const int u0 = parts_before(p.seq_lens, p.qsl, s);
+  for (int g = 0; g < G; ++g) {
+    float M = -INFINITY;
+    for (int q = 0; q < nparts; ++q) M = fmaxf(M, p.ws_ml[(((size_t)(u0 + q)) * hq + kvh * G + g) * 2]);
+    float den = 0.f;
+    float num[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) num[j] = 0.f;
+    for (int q = 0; q < nparts; ++q) {
+      const size_t w = ((size_t)(u0 + q)) * hq + (size_t)kvh * G + g;
+      const float sc = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M);
+      den = fmaf(sc, p.ws_ml[w * 2 + 1], den);
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) num[j] = fmaf(sc, p.ws_acc[w * D + j * 64 + lane], num[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+  }
+}
+
+template <int ES, int D, int G>
+static hipError_t decode_rows_t(const DecodeParams& p, int64_t units, int num_seqs, int hkv,
+                                hipStream_t stream) {
+  if (units > 0)
+    hipLaunchKernelGGL((k_decode_partition<ES, D, G>), dim3((unsigned)(units * hkv)), dim3(64), 0,
+                       stream, p);
+  if (num_seqs > 0)
+    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((int64_t)num_seqs * hkv)), dim3(64),
+                       0, stream, p);
+  return hipGetLastError();
+}
+
+template <int ES, int D>
+static hipError_t decode_rows_g(int G, const DecodeParams& p, int64_t units, int num_seqs, int hkv,
+                                hipStream_t stream) {
+  switch (G) {
+    case 1: return decode_rows_t<ES, D, 1>(p, units, num_seqs, hkv, stream);
+    case 2: return decode_rows_t<ES, D, 2>(p, units, num_seqs, hkv, stream);
+    case 4: return decode_rows_t<ES, D, 4>(p, units, num_seqs, hkv, stream);
+    case 8: return decode_rows_t<ES, D, 8>(p, units, num_seqs, hkv, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  DecodeParams p;
+  p.kv = c.kv;
+  p.block_bytes = c.block_bytes;
+  p.hkv = c.hkv;
+  p.q = a.q;
+  p.out = a.out;
+  p.block_tables = a.block_tables;
+  p.max_blocks = a.max_blocks;
+  p.seq_lens = a.seq_lens;
+  p.qsl = a.query_start_loc;
+  p.num_seqs = a.num_seqs;
+  p.scale_log2 = a.scale * kLog2e;
+  p.ws_acc = a.ws_acc;
+  p.ws_ml = a.ws_ml;
+  const int G = a.hq / c.hkv;
+  if (c.dtype_bytes == 4) {
+    if (c.head_size == 64) return decode_rows_g<4, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);
+    if (c.head_size == 128) return decode_rows_g<4, 128>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);
+  } else {
+    if (c.head_size == 64) return decode_rows_g<2, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);
+    if (c.head_size == 128) return decode_rows_g<2, 128>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_rows(const CacheDesc&, const AttnDesc& a, hipStream_t) {
+  return a.prefill_tiles > 0 ? hipErrorNotSupported : hipSuccess;
+}
+
+}  // namespace pkv

@@ -1,0 +1,165 @@
+"""Parity of the HIP path with the fp64 oracle, on the GPU.
+
+Bars: KV writes, block copies, slots and tables bit-exact; attention within
+max|d| <= 5e-3 and relative L2 <= 1e-3 for bf16 inputs (fp32 accumulation),
+and within 1e-5 for the fp32 tiny decode.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import paged_oracle as po
+from oracle import scenario
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from paged_kv_attention_06_amd import step as gpu_step  # noqa: E402
+
+MAX_ABS_BF16, REL_L2_BF16 = 5e-3, 1e-3
+MAX_ABS_F32 = 1e-5
+
+
+def _announce(what):
+    print(f"\n[gpu case] {what}", file=sys.stderr, flush=True)
+
+
+def _check_attention(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    assert np.all(np.isfinite(gpu)), f"{what}: non-finite output"
+    diff = np.abs(gpu.astype(np.float64) - ref)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    rel = float(np.linalg.norm(gpu.astype(np.float64) - ref) / max(np.linalg.norm(ref), 1e-30))
+    if dtype == "f32":
+        assert max_abs <= MAX_ABS_F32, f"{what}: max|d| {max_abs:.3e}"
+    else:
+        assert max_abs <= MAX_ABS_BF16, f"{what}: max|d| {max_abs:.3e}"
+        assert rel <= REL_L2_BF16, f"{what}: rel L2 {rel:.3e}"
+    return max_abs, rel
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5, 4])
+def test_small_workload_full_parity(cfg):
+    """Whole pool bit-exact and every output row within tolerance."""
+    w = workloads.small(cfg)
+    _announce(f"small config {cfg}: B={w.batch} T={w.num_tokens} L={w.seq_lens.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.h_slots, ref["slots"])
+    assert np.array_equal(st.h_cow, ref["cow_pairs"])
+    pool = st.pool_codes()
+    assert np.array_equal(pool, ref["pool"]), "pool differs from the oracle's"
+    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"small config {cfg}")
+
+
+def _sample_seqs(w, k=6, seed=0):
+    rng = np.random.default_rng(seed)
+    L = w.seq_lens
+    picks = {int(np.argmax(L)), int(np.argmin(L)), 0, w.batch - 1}
+    picks.update(int(i) for i in rng.choice(w.batch, size=min(k, w.batch), replace=False))
+    if np.any(w.fork_of >= 0):
+        picks.add(int(np.flatnonzero(w.fork_of >= 0)[0]))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5, 4])
+def test_full_size_sampled_parity(cfg):
+    """Full-size workload in the bench's launch configuration; sampled rows
+    against the oracle, plus the step's written slots and COW copies."""
+    w = workloads.make(cfg)
+    _announce(f"full config {cfg}: B={w.batch} T={w.num_tokens} blocks={w.num_blocks}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    assert np.all(np.isfinite(out)), "non-finite output"
+    qsl = w.query_start_loc
+    got, want = [], []
+    for s in _sample_seqs(w):
+        q_len = int(w.q_len[s])
+        rows = list(range(q_len)) if q_len <= 8 else [0, 1, q_len // 2, q_len - 2, q_len - 1]
+        ref = scenario.sequence_attention(w, s, rows)
+        got.append(out[qsl[s] + np.asarray(rows)])
+        want.append(ref)
+    _check_attention(np.concatenate(got), np.concatenate(want), w.dtype, f"full config {cfg}")
+
+    # the step's written tokens sit at the oracle's slots with their drawn values
+    tabs = scenario.build_tables(w, with_pool=False)
+    assert np.array_equal(st.h_slots, tabs["slots"])
+    assert np.array_equal(st.h_cow, tabs["cow_pairs"])
+    kidx = po.k_tile_index(w.head_size, w.dtype)
+    vidx = po.v_tile_index(w.head_size, w.dtype)
+    code = np.uint16 if w.dtype == "bf16" else np.uint32
+    bb = 2 * 16 * w.num_kv_heads * w.head_size * w.dtype_bytes
+    kv = st.kv.view(-1)
+    pick = np.unique(np.linspace(0, len(tabs["slots"]) - 1, 16).astype(int))
+    for t in pick:
+        slot = int(tabs["slots"][t])
+        blk, off = divmod(slot, 16)
+        raw = kv[blk * bb:(blk + 1) * bb].cpu().numpy().view(code)
+        raw = raw.reshape(w.num_kv_heads, 2, 16 * w.head_size)
+        assert np.array_equal(raw[:, 0, kidx[off]], w.new_k[t]), f"K of token {t}"
+        assert np.array_equal(raw[:, 1, vidx[off]], w.new_v[t]), f"V of token {t}"
+    # a COW destination holds the source's first (partial) tokens
+    for src, dst in tabs["cow_pairs"][:3]:
+        a = kv[src * bb:(src + 1) * bb].cpu().numpy().view(code).reshape(w.num_kv_heads, 2, -1)
+        b = kv[dst * bb:(dst + 1) * bb].cpu().numpy().view(code).reshape(w.num_kv_heads, 2, -1)
+        n_old = int(w.prompt_len[0]) % 16
+        for off in range(n_old):
+            assert np.array_equal(a[:, 0, kidx[off]], b[:, 0, kidx[off]])
+            assert np.array_equal(a[:, 1, vidx[off]], b[:, 1, vidx[off]])
+
+
+def test_decode_is_deterministic_and_layout_invariant():
+    """Two runs give identical bits; moving every block to another physical
+    id (a different free order) gives identical bits too."""
+    w = workloads.small(3)
+    _announce("determinism / block permutation, small config 3")
+    a = gpu_step.run_workload(w).out.cpu().numpy()
+    b = gpu_step.run_workload(w).out.cpu().numpy()
+    assert np.array_equal(a, b)
+    w2 = workloads.small(3)
+    w2.free_order = np.random.default_rng(99).permutation(w2.num_blocks).astype(np.int32)
+    c = gpu_step.run_workload(w2).out.cpu().numpy()
+    assert np.array_equal(a, c)
+
+
+def test_empty_sequence_row_is_zero():
+    w = workloads.small(3)
+    w.hist_len = w.hist_len.copy()
+    _announce("empty decode row")
+    st = gpu_step.PagedStep(w)
+    st.build_history()
+    st.prepare_step()
+    st.copy_and_write()
+    st.h_seq_lens = st.h_seq_lens.copy()
+    st.h_seq_lens[1] = 0
+    st.seq_lens = torch.from_numpy(st.h_seq_lens).cuda()
+    st.out.fill_(7.0)
+    st.attend()
+    torch.cuda.synchronize()
+    out = st.out.cpu().numpy()
+    assert np.all(out[1] == 0)
+    ref = scenario.run_step(w)["out"]
+    keep = [s for s in range(w.batch) if s != 1]
+    _check_attention(out[keep], ref[keep], w.dtype, "rows next to an empty one")
+
+
+def test_split_boundaries():
+    """Lengths at and around the 256-token partition and 16-token block edges."""
+    lens = [1, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1024, 1025]
+    w = workloads.small(3)
+    B = len(lens)
+    rng = np.random.default_rng(5)
+    L = np.asarray(lens, np.int32)
+    w2 = workloads._build(3, "split edges", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                          np.ones(B, np.int32), 400, [rng, np.random.default_rng(6),
+                                                       np.random.default_rng(7), rng])
+    _announce(f"split boundaries L={lens}")
+    st = gpu_step.run_workload(w2)
+    ref = scenario.run_step(w2)
+    assert np.array_equal(st.pool_codes(), ref["pool"])
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", "split boundaries")
+    del w

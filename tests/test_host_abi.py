@@ -1,0 +1,186 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+and its host-side work (slot mapping, block allocator, argument checks,
+sizing) agrees exactly with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import paged_oracle as po
+from oracle import scenario
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = pytest.importorskip("paged_kv_attention_06_amd")
+from paged_kv_attention_06_amd import _lib as L  # noqa: E402
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keywords = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in keywords})
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    declared = _declared_functions()
+    assert len(declared) >= 17
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(L.EXPORTED)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_block_bytes_per_config(cfg):
+    w = workloads.small(cfg)
+    d = P.descriptor(7, w.num_kv_heads, w.head_size, P.PKV_F32 if w.dtype == "f32" else P.PKV_BF16)
+    assert P.pkv_block_bytes(d) == po.block_bytes(16, w.num_kv_heads, w.head_size, w.dtype_bytes)
+
+
+def test_block_bytes_rejects_bad_descriptors():
+    assert P.pkv_block_bytes(P.descriptor(7, 8, 96, P.PKV_BF16)) == 0     # head size
+    assert P.pkv_block_bytes(P.descriptor(7, 8, 128, 9)) == 0             # dtype
+    assert P.pkv_block_bytes(P.descriptor(7, 8, 128, P.PKV_BF16, block_size=32)) == 0
+    assert P.pkv_block_bytes(P.descriptor(0, 8, 128, P.PKV_BF16)) == 0
+
+
+def _gpu_side_tables(w):
+    """Replays allocation with the library's pkv_pool (host only)."""
+    pool = P.Pool(w.num_blocks, w.free_order)
+    maxb = max(1, -(-int(w.seq_lens.max()) // 16))
+    tables = np.zeros((w.batch, maxb), np.int32)
+    prompts = []
+    for p in range(len(w.prompt_len)):
+        t = np.zeros(maxb, np.int32)
+        pool.append(t, 0, int(w.prompt_len[p]))
+        prompts.append(t)
+    for s in range(w.batch):
+        if w.fork_of[s] < 0:
+            pool.append(tables[s], 0, int(w.hist_len[s]))
+    for s in range(w.batch):
+        if w.fork_of[s] >= 0:
+            p = int(w.fork_of[s])
+            nb = -(-int(w.prompt_len[p]) // 16)
+            tables[s, :nb] = pool.fork(prompts[p], nb)[:nb]
+    if not w.prompt_owner_keeps_ref:
+        for p, t in enumerate(prompts):
+            pool.release(t, -(-int(w.prompt_len[p]) // 16))
+    slots, cows = [], []
+    for s in range(w.batch):
+        sl, c = pool.append(tables[s], int(w.hist_len[s]), int(w.q_len[s]))
+        slots.append(sl)
+        if c is not None:
+            cows.append(c)
+    return pool, tables, np.concatenate(slots), np.asarray(cows, np.int64).reshape(-1, 2), prompts
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_allocator_matches_oracle_small(cfg):
+    w = workloads.small(cfg)
+    pool, tables, slots, cows, prompts = _gpu_side_tables(w)
+    st = scenario.build_tables(w, with_pool=False)
+    for s in range(w.batch):
+        n = len(st["tables"][s])
+        assert tables[s, :n].tolist() == st["tables"][s]
+    assert np.array_equal(slots, st["slots"])
+    assert np.array_equal(cows, st["cow_pairs"])
+    assert pool.num_free() == st["alloc"].num_free()
+    for b in range(w.num_blocks):
+        assert pool.refcnt(b) == st["alloc"].ref[b]
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_allocator_and_slots_match_oracle_full_size(cfg):
+    w = workloads.make(cfg, values=False)
+    pool, tables, slots, cows, _ = _gpu_side_tables(w)
+    st = scenario.build_tables(w, with_pool=False)
+    for s in range(w.batch):
+        n = len(st["tables"][s])
+        assert tables[s, :n].tolist() == st["tables"][s]
+    assert np.array_equal(slots, st["slots"])
+    assert np.array_equal(cows, st["cow_pairs"])
+    # the library's slot builder agrees with the allocator's slots and the oracle's
+    lib_slots = P.pkv_build_slot_mapping(tables, w.query_start_loc, w.seq_lens)
+    assert np.array_equal(lib_slots, slots)
+    bt = scenario.table_matrix(st["tables"], tables.shape[1])
+    assert np.array_equal(po.slot_mapping(bt, w.query_start_loc, w.seq_lens), lib_slots)
+
+
+def test_cow_walkthrough_through_library():
+    pool = P.Pool(10, np.array([0, 1, 2, 7, 3, 4, 5, 6, 8, 9], np.int32))
+    prompt = np.zeros(4, np.int32)
+    pool.append(prompt, 0, 40)
+    assert prompt[:3].tolist() == [0, 1, 2]
+    samples = [prompt] + [pool.fork(prompt, 3) for _ in range(3)]
+    assert [pool.refcnt(b) for b in (0, 1, 2)] == [4, 4, 4]
+    slots, cow = pool.append(samples[0], 40, 1)
+    assert cow == (2, 7) and samples[0][:3].tolist() == [0, 1, 7] and pool.refcnt(2) == 3
+    assert slots.tolist() == [7 * 16 + 8]
+
+
+def test_allocator_errors_leave_state_unchanged():
+    pool = P.Pool(3)
+    t = np.zeros(8, np.int32)
+    with pytest.raises(P.PkvError) as e:
+        pool.append(t, 0, 60)                       # 4 blocks > 3 free
+    assert e.value.status == 6
+    assert pool.num_free() == 3
+    with pytest.raises(P.PkvError) as e:
+        pool.append(np.zeros(2, np.int32), 0, 40)   # table capacity
+    assert e.value.status == 7
+    with pytest.raises(P.PkvError):
+        P.Pool(3, np.array([0, 0, 1], np.int32))    # not a permutation
+
+
+def test_slot_mapping_rejects_bad_lengths():
+    bt = np.array([[3, 4]], np.int32)
+    with pytest.raises(P.PkvError) as e:
+        P.pkv_build_slot_mapping(bt, [0, 1], [33])  # longer than the table
+    assert e.value.status == 7
+    with pytest.raises(P.PkvError):
+        P.pkv_build_slot_mapping(bt, [0, 3], [2])   # more rows than tokens
+    assert P.pkv_build_slot_mapping(bt, [0, 2], [18]).tolist() == [4 * 16 + 0, 4 * 16 + 1]
+
+
+def test_page_address_translation_through_library():
+    bt = np.array([[17, 42, 99]], np.int32)
+    assert P.pkv_build_slot_mapping(bt, [0, 1], [19]).tolist() == [42 * 16 + 2]
+
+
+def test_workspace_sizing():
+    d = P.descriptor(100, 8, 128, P.PKV_BF16)
+    cache = P.Cache(None, 100, 8, 128, P.PKV_BF16)
+    cache.desc = d
+    lens = np.array([1, 256, 257, 0, 8192], np.int32)
+    units = 1 + 1 + 2 + 0 + 32
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens) == units * 32 * (128 + 2) * 4
+    qsl = np.array([0, 1, 2, 3, 3, 1000], np.int32)   # seq 4 is a prefill chunk
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == 4 * 32 * 130 * 4
+
+
+def _call_decode(cache_desc, out=1, q=1, bt=1, sl=1, h_sl=None, n=1, hq=32, ws=None, ws_bytes=0,
+                 maxb=4):
+    h_sl = np.array([5], np.int32) if h_sl is None else h_sl
+    return L._c["paged_attention_decode"](
+        ctypes.byref(cache_desc), out, q, hq, bt, maxb, sl,
+        h_sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, 0.1, ws, ws_bytes, None)
+
+
+def test_argument_checks_return_before_launch():
+    good = P.descriptor(16, 8, 128, P.PKV_BF16, kv_ptr=0x1000)
+    assert _call_decode(P.descriptor(16, 8, 128, P.PKV_BF16)) == 1          # NULL pool
+    assert _call_decode(P.descriptor(16, 8, 96, P.PKV_BF16, kv_ptr=0x1000)) == 2
+    assert _call_decode(P.descriptor(16, 8, 128, 7, kv_ptr=0x1000)) == 3
+    assert _call_decode(good, hq=12) == 2                                   # 12 % 8 != 0
+    assert _call_decode(good, hq=8 * 16) == 2                               # group of 16
+    assert _call_decode(good, h_sl=np.array([65], np.int32)) == 7          # > 4 blocks
+    assert _call_decode(good, out=None) == 1
+    assert _call_decode(good, h_sl=np.array([300], np.int32), maxb=32) == 4  # needs workspace
+    st = L._c["paged_kv_write"](ctypes.byref(good), None, None, None, 5, None)
+    assert st == 1
+    assert L._c["paged_kv_write"](ctypes.byref(good), None, None, None, 0, None) == 0
+    assert L._c["block_copy"](ctypes.byref(good), None, -1, None) == 2

@@ -96,7 +96,9 @@ def _bf16_codes(x: np.ndarray) -> np.ndarray:
     return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
 
 
-def _values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+def _values(rng: np.random.Generator, shape, dtype: str, draw: bool = True) -> np.ndarray:
+    if not draw:
+        return np.zeros(shape, dtype=np.uint32 if dtype == "f32" else np.uint16)
     if dtype == "f32":
         return rng.uniform(-1.0, 1.0, size=shape).astype(np.float32).view(np.uint32)
     out = np.empty(shape, dtype=np.uint16)
@@ -115,7 +117,7 @@ def _pool_size(lengths, factor: float, extra_blocks: int = 0) -> int:
 
 def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, scale: float,
            hist_len, q_len, num_blocks: int, streams, fork_of=None, prompt_len=(),
-           owner_ref=False, extra=None) -> Workload:
+           owner_ref=False, extra=None, values: bool = True) -> Workload:
     _, r_blocks, r_vals, _ = streams
     hist_len = np.asarray(hist_len, dtype=np.int32)
     q_len = np.asarray(q_len, dtype=np.int32)
@@ -134,24 +136,26 @@ def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, sca
         head_size=D, scale=scale, num_blocks=num_blocks, free_order=free_order,
         hist_len=hist_len, q_len=q_len, fork_of=fork_of, prompt_len=prompt_len,
         prompt_owner_keeps_ref=owner_ref,
-        hist_k=_values(r_vals, (n_hist, Hkv, D), dtype),
-        hist_v=_values(r_vals, (n_hist, Hkv, D), dtype),
+        hist_k=_values(r_vals, (n_hist, Hkv, D), dtype, values),
+        hist_v=_values(r_vals, (n_hist, Hkv, D), dtype, values),
         hist_start=hist_start,
-        prompt_k=_values(r_vals, (n_prompt, Hkv, D), dtype),
-        prompt_v=_values(r_vals, (n_prompt, Hkv, D), dtype),
+        prompt_k=_values(r_vals, (n_prompt, Hkv, D), dtype, values),
+        prompt_v=_values(r_vals, (n_prompt, Hkv, D), dtype, values),
         prompt_start=prompt_start,
-        new_k=_values(r_vals, (T, Hkv, D), dtype),
-        new_v=_values(r_vals, (T, Hkv, D), dtype),
-        q=_values(r_vals, (T, Hq, D), dtype),
+        new_k=_values(r_vals, (T, Hkv, D), dtype, values),
+        new_v=_values(r_vals, (T, Hkv, D), dtype, values),
+        q=_values(r_vals, (T, Hq, D), dtype, values),
         pool_fill=F32_NAN if dtype == "f32" else BF16_NAN,
         extra=extra or {},
     )
     return w
 
 
-def make(config_id: int, seed: int = 0, batch: int | None = None) -> Workload:
+def make(config_id: int, seed: int = 0, batch: int | None = None, values: bool = True) -> Workload:
     """The workload of one configuration.  ``batch`` (optional) keeps the
-    shape and length distribution but draws fewer sequences, for quick runs."""
+    shape and length distribution but draws fewer sequences, for quick runs.
+    ``values=False`` skips drawing K/V/Q (zeros instead); lengths and block
+    order are unchanged."""
     streams = np.random.SeedSequence(config_id + 1000 * seed).spawn(4)
     streams = [np.random.default_rng(s) for s in streams]
     r_len = streams[0]
@@ -159,20 +163,20 @@ def make(config_id: int, seed: int = 0, batch: int | None = None) -> Workload:
     if config_id == 1:
         L = np.array([5, 16, 17, 40], np.int32)
         return _build(1, "tiny decode", "f32", 4, 4, 64, 1.0 / 8.0, L - 1, np.ones(4, np.int32),
-                      64, streams)
+                      64, streams, values=values)
 
     if config_id == 2:
         B = batch or 64
         L = r_len.integers(128, 2048, size=B, endpoint=True).astype(np.int32)
         return _build(2, "7B MHA decode", "bf16", 32, 32, 128, 128 ** -0.5, L - 1,
-                      np.ones(B, np.int32), _pool_size(L, 1.25), streams)
+                      np.ones(B, np.int32), _pool_size(L, 1.25), streams, values=values)
 
     if config_id == 3:
         B = batch or 256
         L = np.rint(r_len.lognormal(np.log(800.0), 1.0, size=B))
         L = np.clip(L, 16, 8192).astype(np.int32)
         return _build(3, "8B GQA decode", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
-                      np.ones(B, np.int32), 200_000, streams)
+                      np.ones(B, np.int32), 200_000, streams, values=values)
 
     if config_id == 4:
         n_dec = 98 if batch is None else max(batch - 1, 1)
@@ -181,7 +185,7 @@ def make(config_id: int, seed: int = 0, batch: int | None = None) -> Workload:
         hist = np.concatenate([L_dec - 1, [cached]]).astype(np.int32)
         qlen = np.concatenate([np.ones(n_dec, np.int32), [chunk]]).astype(np.int32)
         return _build(4, "mixed chunked prefill + decode", "bf16", 32, 8, 128, 128 ** -0.5,
-                      hist, qlen, _pool_size(hist + qlen, 1.25), streams)
+                      hist, qlen, _pool_size(hist + qlen, 1.25), streams, values=values)
 
     if config_id == 5:
         n_fork = 16 if batch is None else max(batch // 2, 1)
@@ -195,7 +199,7 @@ def make(config_id: int, seed: int = 0, batch: int | None = None) -> Workload:
         lengths = list(L_ind) + [prompt]
         return _build(5, "13B MHA prefix sharing + long context", "bf16", 40, 40, 128,
                       128 ** -0.5, hist, qlen, _pool_size(lengths, 1.25, extra_blocks=n_fork),
-                      streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True)
+                      streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True, values=values)
 
     raise ValueError(f"unknown config {config_id}")
 
