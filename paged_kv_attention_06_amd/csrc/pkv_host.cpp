@@ -75,7 +75,7 @@ struct Plan {
 
 // Validates host lengths and counts the work.  qsl may be NULL (decode).
 int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs,
-                   int32_t max_blocks, Plan* plan) {
+                   int32_t max_blocks, int group, Plan* plan) {
   if (!seq_lens) return fail(PKV_ERR_NULL, "host seq_lens is NULL");
   if (num_seqs < 0) return fail(PKV_ERR_DIM, "num_seqs %d < 0", num_seqs);
   if (max_blocks < 0) return fail(PKV_ERR_DIM, "max_blocks_per_seq %d < 0", max_blocks);
@@ -94,7 +94,8 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
     if (ql == 1) {
       if (L > 0) plan->decode_units += (L + pkv::kPartTokens - 1) / pkv::kPartTokens;
     } else if (ql > 1) {
-      plan->prefill_tiles += (ql + pkv::kPrefillTileQ - 1) / pkv::kPrefillTileQ;
+      const int tq = pkv::prefill_tile_q(group);
+      plan->prefill_tiles += (ql + tq - 1) / tq;
       plan->prefill_seqs += 1;
     }
     plan->num_tokens += ql;
@@ -121,8 +122,12 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
                 num_q_heads / c.hkv);
   if (mixed && !h_qsl) return fail(PKV_ERR_NULL, "host query_start_loc is NULL");
   Plan plan;
-  if (int e = plan_attention(mixed ? h_qsl : nullptr, h_seq_lens, num_seqs, max_blocks, &plan))
+  if (int e = plan_attention(mixed ? h_qsl : nullptr, h_seq_lens, num_seqs, max_blocks,
+                             num_q_heads / c.hkv, &plan))
     return e;
+  if (plan.prefill_tiles > 0 && !pkv::prefill_supported(num_q_heads / c.hkv, c.dtype_bytes))
+    return fail(PKV_ERR_DTYPE,
+                "rows with q_len > 1 need a bf16 cache and 1, 2 or 4 query heads per kv head");
   if (mixed && plan.num_tokens != num_tokens)
     return fail(PKV_ERR_RANGE, "query_start_loc[num_seqs] = %lld but num_tokens = %lld",
                 (long long)plan.num_tokens, (long long)num_tokens);
@@ -242,7 +247,10 @@ size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads
   pkv::CacheDesc c;
   if (check_cache(cache, &c, false) || num_q_heads < 1) return 0;
   Plan plan;
-  if (plan_attention(h_qsl, h_seq_lens, num_seqs, INT32_MAX / pkv::kBlockSize, &plan)) return 0;
+  if (num_q_heads % c.hkv != 0 || !pkv::supported_group(num_q_heads / c.hkv)) return 0;
+  if (plan_attention(h_qsl, h_seq_lens, num_seqs, INT32_MAX / pkv::kBlockSize,
+                     num_q_heads / c.hkv, &plan))
+    return 0;
   return workspace_for(plan, num_q_heads, c.head_size);
 }
 

@@ -11,9 +11,9 @@ constexpr int kBlockSize = 16;
 // Split-K partition length of the decode kernel, in tokens (a multiple of
 // the 64 tokens one wave covers per step).  The workspace size depends on it.
 constexpr int kPartTokens = 256;
-// Query positions per prefill tile (each tile also packs every query head of
-// one kv-head group into its rows).
-constexpr int kPrefillTileQ = 16;
+// Query positions per prefill workgroup: its 4 waves of 32 query rows cover
+// the G query heads of one kv head, so 128 / G positions.
+constexpr int prefill_tile_q(int g) { return 128 / g; }
 
 struct CacheDesc {
   char* kv;
@@ -52,5 +52,9 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
 hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 
 bool supported_group(int g);
+// Group sizes the mixed path's prefill rows support (bf16 caches only).
+inline bool prefill_supported(int g, int dtype_bytes) {
+  return dtype_bytes == 2 && (g == 1 || g == 2 || g == 4);
+}
 
 }  // namespace pkv

@@ -553,8 +553,318 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_prefill_rows(const CacheDesc&, const AttnDesc& a, hipStream_t) {
-  return a.prefill_tiles > 0 ? hipErrorNotSupported : hipSuccess;
+// ---------------------------------------------------------------------------
+// Prefill rows of a mixed batch (chunked prefill, juhe.plus section 4.2):
+// sequence s has q_len > 1 query rows at positions L - q_len .. L - 1, each
+// seeing keys 0..its position.  Both products are dense here, so they run
+// on MFMA (v_mfma_f32_32x32x16_bf16):
+//   S^T = K Q^T   (32 keys x 32 query rows per tile, k = head dim)
+//   O^T += V^T P^T (32 d x 32 query rows, k = keys)
+// Computing S transposed leaves each lane with one query row, so the
+// softmax row max needs a single exchange between the two 32-lane halves,
+// and the S^T accumulator is already the B operand of the second product.
+// P is split into bf16 hi + lo parts (two MFMAs) so probabilities keep
+// about 16 significant bits; V enters exactly.
+// One workgroup = 4 waves = one kv head x TQ positions; wave w takes query
+// head w % G of the group and positions 32*(w / G) .. +31 of the tile.
+// Keys arrive 64 at a time (4 blocks) through the block table into LDS,
+// K as [key][d] and V as [d][key].
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct PrefillParams {
+  const char* kv;
+  size_t block_bytes;
+  int hkv;
+  const uint16_t* q;
+  float* out;
+  const int32_t* block_tables;
+  int max_blocks;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int num_seqs;
+  float scale_log2;
+};
+
+template <int D, int G>
+struct PrefillShape {
+  static constexpr int TQ = prefill_tile_q(G);  // query positions per workgroup
+  static constexpr int KT = 64;                 // keys per LDS tile (4 blocks)
+  static constexpr int KROW = D * 2 + 16;       // LDS bytes per key row of K (padded)
+  static constexpr int VROW = KT * 2 + 16;      // LDS bytes per d row of V^T (padded)
+  static constexpr int KS = D / 16;             // MFMA k-steps over the head dim
+  static constexpr int DB = D / 32;             // 32-row d blocks of O^T
+  static constexpr int TILE = BS * D * 2;       // bytes of one K or V tile in HBM
+};
+
+// Find (sequence, item, items of that sequence) of work item u, where
+// count(s) gives the items of sequence s.  Every lane gets the result.
+template <typename F>
+__device__ bool find_item(int u, int num_seqs, F count, int& s_out, int& item_out, int& n_out) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int s0 = 0; s0 < num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    const int n = (s < num_seqs) ? count(s) : 0;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const int total = __shfl(incl, 63);
+    if (u < base + total) {
+      const unsigned long long m = __ballot(base + incl > u);
+      const int ls = __ffsll((unsigned long long)m) - 1;
+      const int incl_s = __shfl(incl, ls);
+      const int n_s = __shfl(n, ls);
+      s_out = uniform(s0 + ls);
+      item_out = uniform(u - (base + incl_s - n_s));
+      n_out = uniform(n_s);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
+  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_prefill_tile(PrefillParams p) {
+  using S = PrefillShape<D, G>;
+  static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
+  __shared__ __align__(16) char k_lds[S::KT * S::KROW];
+  __shared__ __align__(16) char v_lds[D * S::VROW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kvh = blockIdx.x % p.hkv;
+  const int item = blockIdx.x / p.hkv;
+  int s, tile, ntiles;
+  const int32_t* qsl = p.qsl;
+  auto tiles_of = [qsl](int q) {
+    const int ql = qsl[q + 1] - qsl[q];
+    return ql > 1 ? (ql + S::TQ - 1) / S::TQ : 0;
+  };
+  if (!find_item(item, p.num_seqs, tiles_of, s, tile, ntiles)) return;
+  tile = ntiles - 1 - tile;  // later tiles see more keys: dispatch them first
+
+  const int hq = p.hkv * G;
+  const int L = p.seq_lens[s];
+  const int row0 = qsl[s];
+  const int ql = qsl[s + 1] - row0;
+  const int qfirst = L - ql;                       // position of query row 0
+  const int p0 = qfirst + tile * S::TQ;
+  const int pend = min(qfirst + ql, p0 + S::TQ);   // positions [p0, pend)
+  const int g = wave % G;
+  const int wp0 = p0 + 32 * (wave / G);
+  const int wlast = min(wp0 + 31, pend - 1);       // < wp0 when the wave has no rows
+  const int h = lane >> 5;
+  const int r = lane & 31;
+  const int my_pos = wp0 + r;
+  const bool row_ok = my_pos < pend;
+  const int head = kvh * G + g;
+
+  // Q^T operand: lane (h, r) holds q[row r][16 ks + 8 h .. + 8] for every ks.
+  bf16x8_t qb[S::KS];
+  {
+    const size_t tok = (size_t)row0 + (size_t)(row_ok ? my_pos - qfirst : 0);
+    const uint4* qrow = reinterpret_cast<const uint4*>(p.q + (tok * hq + head) * D);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const uint4 v = row_ok ? qrow[2 * ks + h] : make_uint4(0, 0, 0, 0);
+      qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x16_t o[S::DB];
+#pragma unroll
+  for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
+  float m_run = -1e30f;
+  float l_run = 0.f;
+
+  const int kend = pend;                 // keys 0 .. pend - 1 are needed
+  const int nkt = (kend + S::KT - 1) / S::KT;
+  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
+  const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * S::KT;
+    __syncthreads();  // the previous tile is consumed
+    // ---- gather 4 blocks' K and V through the block table into LDS
+    constexpr int KGR = 2 * D;  // 16-byte granules per K (or V) tile
+#pragma unroll
+    for (int gi = tid; gi < 4 * KGR; gi += 256) {
+      const int bl = gi / KGR;
+      const int blk = kt * 4 + bl;
+      const bool valid = blk * BS < kend;
+      const int within = gi % KGR;
+      if (valid) {
+        const int phys = bt[blk];
+        const char* base = head_base + (size_t)phys * p.block_bytes;
+        {  // K granule (c, t): 8 consecutive d of token t
+          const int c = within / BS, t = within % BS;
+          const uint4 v = *reinterpret_cast<const uint4*>(base + (c * BS + t) * 16);
+          *reinterpret_cast<uint4*>(k_lds + (bl * BS + t) * S::KROW + c * 16) = v;
+        }
+        {  // V granule (kg, d): 8 consecutive keys of one d
+          const int kg = within / D, d = within % D;
+          uint4 v = *reinterpret_cast<const uint4*>(base + S::TILE + (kg * D + d) * 16);
+          const int key0 = blk * BS + kg * 8;
+          if (key0 + 8 > L) {  // keys at or past L were never written: zero them
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) = v;
+        }
+      } else {
+        const int kg = within / D, d = within % D;
+        *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) =
+            make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (k0 > wlast) continue;  // every key of the tile is after this wave's rows
+
+    // ---- S^T for two 32-key sub-tiles
+    f32x16_t sacc[2];
+    float x[2][16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kj = k0 + 32 * j;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[j][i] = 0.f;
+      if (kj <= wlast) {
+        const char* krow = k_lds + (32 * j + r) * S::KROW + h * 16;
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) {
+          const uint4 a = *reinterpret_cast<const uint4*>(krow + ks * 32);
+          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks],
+                                                            sacc[j], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kj + 8 * (i >> 2) + 4 * h + (i & 3);
+        const bool ok = row_ok && kj <= wlast && key <= my_pos;
+        x[j][i] = ok ? sacc[j][i] * p.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[j][i]);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    // ---- lazy rescale of this row's state
+    const bool need = mt > m_run + kRescaleSlack;
+    if (__ballot(need)) {
+      const float corr = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
+      m_run = need ? mt : m_run;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
+    }
+    // ---- probabilities, split into bf16 hi + lo, as the B operand of PV
+    uint32_t phi[2][2][4], plo[2][2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float a = __builtin_amdgcn_exp2f(x[j][8 * kk + 2 * m] - m_run);
+          const float b = __builtin_amdgcn_exp2f(x[j][8 * kk + 2 * m + 1] - m_run);
+          l_run += a + b;
+          const float ah = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
+          const float bh = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
+          phi[j][kk][m] = pack_hi(ah, bh);
+          plo[j][kk][m] = pack_hi(a - ah, b - bh);
+        }
+      }
+    }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (k0 + 32 * j > wlast) continue;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8_t bh = __builtin_bit_cast(
+            bf16x8_t, make_uint4(phi[j][kk][0], phi[j][kk][1], phi[j][kk][2], phi[j][kk][3]));
+        const bf16x8_t bl = __builtin_bit_cast(
+            bf16x8_t, make_uint4(plo[j][kk][0], plo[j][kk][1], plo[j][kk][2], plo[j][kk][3]));
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          const char* vrow = v_lds + (32 * db + r) * S::VROW + (32 * j + 16 * kk + 4 * h) * 2;
+          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16);
+          const bf16x8_t a =
+              __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, o[db], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    float* orow = p.out + (((size_t)row0 + (my_pos - qfirst)) * hq + head) * D;
+    const float inv = 1.f / l_tot;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * h;
+        *reinterpret_cast<float4*>(orow + d) =
+            make_float4(o[db][4 * i4] * inv, o[db][4 * i4 + 1] * inv, o[db][4 * i4 + 2] * inv,
+                        o[db][4 * i4 + 3] * inv);
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill_tile<D, 4>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  if (a.prefill_tiles == 0) return hipSuccess;
+  if (c.dtype_bytes != 2) return hipErrorInvalidValue;
+  PrefillParams p;
+  p.kv = c.kv;
+  p.block_bytes = c.block_bytes;
+  p.hkv = c.hkv;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.out = a.out;
+  p.block_tables = a.block_tables;
+  p.max_blocks = a.max_blocks;
+  p.seq_lens = a.seq_lens;
+  p.qsl = a.query_start_loc;
+  p.num_seqs = a.num_seqs;
+  p.scale_log2 = a.scale * kLog2e;
+  const int G = a.hq / c.hkv;
+  const int64_t grid = a.prefill_tiles * c.hkv;
+  if (c.head_size == 128) return prefill_g<128>(G, p, grid, stream);
+  if (c.head_size == 64) return prefill_g<64>(G, p, grid, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv
