@@ -26,6 +26,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
+# HBM bytes one attention call moves on this workload, from rocprofv3
+# FETCH_SIZE (x2.000, the factor a 1 GiB device copy needs) plus WRITE_SIZE
+# (x1.000) of k_decode_partition and k_decode_merge; see
+# profiles/decode_8b_gqa_b256_traffic.md.  Reset to None whenever either
+# kernel changes until the counters are taken again.
+MEASURED_TRAFFIC_BYTES = 1_389_700_000
 
 
 def algorithmic_bytes(w) -> int:
@@ -40,9 +46,10 @@ def algorithmic_bytes(w) -> int:
     return kv + q + out + tables + 4 * w.batch
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
+def cpu_baseline(w, min_s: float = 10.0):
     """The oracle (unchanged) on the host: textbook fp64 attention of whole
-    decode rows, one sequence at a time, single-threaded BLAS."""
+    decode rows, one sequence at a time, single-threaded BLAS, repeated over
+    the batch until at least ``min_s`` seconds of work are done."""
     from threadpoolctl import threadpool_limits
 
     from oracle import scenario
@@ -50,15 +57,110 @@ def cpu_baseline(w, budget_s: float = 20.0):
     done_rows = 0
     t0 = time.perf_counter()
     with threadpool_limits(1):
-        for s in order:
-            scenario.sequence_attention(w, int(s))
-            done_rows += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
+        while time.perf_counter() - t0 < min_s:
+            for s in order:
+                scenario.sequence_attention(w, int(s))
+                done_rows += 1
     dt = time.perf_counter() - t0
     return {"value": done_rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_rows} of {w.batch} decode rows of the same workload "
-                      f"(all {w.num_q_heads} heads each), fp64 NumPy, 1 thread, {dt:.1f} s"}
+            "sample": f"{done_rows} decode rows ({done_rows / w.batch:.0f} passes over the "
+                      f"{w.batch}-row batch, all {w.num_q_heads} heads each), fp64 NumPy, "
+                      f"1 thread, {dt:.1f} s"}
+
+
+def prefill_flops(w) -> float:
+    """Multiply-adds of the chunk's unmasked (query, key) pairs, 2 flops
+    each, for Q.K^T and P.V over all query heads."""
+    total = 0.0
+    for s in range(w.batch):
+        ql = int(w.q_len[s])
+        if ql <= 1:
+            continue
+        first = int(w.seq_lens[s]) - ql
+        pairs = sum(first + i + 1 for i in range(ql))
+        total += 4.0 * w.head_size * w.num_q_heads * pairs
+    return total
+
+
+def _timed(fn, steps, warmup, stream, flush=None):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        a, b = ev[i]
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def copy_bandwidth(nbytes=1 << 30):
+    """Device-to-device copy rate on this GPU (read + write bytes / time)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _timed(lambda: dst.copy_(src), 10, 3, torch.cuda.current_stream())
+    return 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+
+
+def run_mixed(args):
+    """Config 4: the whole mixed call, and the prefill chunk alone."""
+    import torch
+
+    import workloads
+    from paged_kv_attention_06_amd import _lib as L
+    from paged_kv_attention_06_amd import step as gpu_step
+
+    w = workloads.make(4)
+    st = gpu_step.PagedStep(w, "cuda")
+    st.build_history()
+    st.prepare_step()
+    st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    mixed_ms = _timed(st.attend, args.steps, args.warmup, stream)
+    # the chunk alone: same call restricted to the prefill sequence
+    s = int(np.argmax(w.q_len))
+    r0, r1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+    sub_qsl = np.array([0, r1 - r0], np.int32)
+    sub_len = w.seq_lens[s:s + 1].astype(np.int32)
+    d_qsl = torch.from_numpy(sub_qsl).cuda()
+    d_len = torch.from_numpy(sub_len).cuda()
+    d_bt = st.block_tables[s:s + 1].contiguous()
+    q = st.q[r0:r1].contiguous()
+    out = torch.empty((r1 - r0, w.num_q_heads, w.head_size), dtype=torch.float32, device="cuda")
+
+    def prefill():
+        L.paged_attention_mixed(st.cache, out, q, d_qsl, d_len, sub_qsl, sub_len, d_bt, w.scale,
+                                None)
+
+    pre_ms = _timed(prefill, args.steps, args.warmup, stream)
+    torch.cuda.synchronize()
+    assert torch.equal(out, st.out[r0:r1]), "prefill-alone rows differ from the mixed call's"
+    flops = prefill_flops(w)
+    pre_mean = float(pre_ms.mean())
+    tflops = flops / (pre_mean * 1e-3) / 1e12
+    mixed_mean = float(mixed_ms.mean())
+    return {
+        "metric": "mixed chunked-prefill step: attention ms and prefill-tile MFMA TFLOP/s",
+        "value": mixed_mean, "unit": "ms", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed_mean,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "8B GQA mixed step: 98 decode rows (contexts U[64,4096]) + one "
+                               "1950-token prefill chunk on 1048 cached tokens, 2048 new tokens"},
+        "prefill_ms": pre_mean,
+        "prefill_gflop": flops / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "traffic": None,
+                     "kernel": "k_prefill_tile (the chunk's rows alone)",
+                     "algorithmic_flops_per_launch": flops},
+    }
 
 
 def main() -> None:
@@ -66,6 +168,9 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", choices=["decode", "mixed"], default="decode",
+                    help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
+                         "prefill step (reported separately)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MiB of scratch between timed steps (0 = back to back)")
@@ -83,6 +188,10 @@ def main() -> None:
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
+
+    if args.workload == "mixed":
+        print(json.dumps(run_mixed(args)), flush=True)
+        return
 
     w = workloads.make(3)
     st = gpu_step.PagedStep(w, "cuda")
@@ -147,6 +256,7 @@ def main() -> None:
         "write_ms": float((step_ms - attn_ms).mean()),
         "hbm_gbps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "device_copy_gbps": copy_bandwidth(),
         "wall_s_timed_region": wall,
         "roofline": {
             "bound": "hbm",
@@ -154,7 +264,7 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": MEASURED_TRAFFIC_BYTES,
             "kernel": "paged_attention_decode (k_decode_partition + k_decode_merge)",
             "algorithmic_bytes_per_launch": alg,
         },

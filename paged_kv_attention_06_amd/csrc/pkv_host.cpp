@@ -68,6 +68,8 @@ int hip_status(hipError_t e, const char* what) {
 
 struct Plan {
   int64_t decode_units = 0;
+  int64_t full_units = 0;
+  int64_t class_count[pkv::kPartClasses] = {0};
   int64_t prefill_tiles = 0;
   int prefill_seqs = 0;
   int64_t num_tokens = 0;
@@ -92,7 +94,12 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
       return fail(PKV_ERR_RANGE, "sequence %d has %lld query rows but length %lld", s,
                   (long long)ql, (long long)L);
     if (ql == 1) {
-      if (L > 0) plan->decode_units += (L + pkv::kPartTokens - 1) / pkv::kPartTokens;
+      if (L > 0) {
+        plan->decode_units += (L + pkv::kPartTokens - 1) / pkv::kPartTokens;
+        plan->full_units += L / pkv::kPartTokens;
+        const int64_t rem = L % pkv::kPartTokens;
+        if (rem) plan->class_count[pkv::kPartClasses - (rem + 31) / 32] += 1;
+      }
     } else if (ql > 1) {
       const int tq = pkv::prefill_tile_q(group);
       plan->prefill_tiles += (ql + tq - 1) / tq;
@@ -104,8 +111,10 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
 }
 
 size_t workspace_for(const Plan& p, int hq, int D) {
-  return (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+  if (p.decode_units == 0) return 0;
+  return pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
 }
+
 
 int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,
               const int32_t* qsl, const int32_t* seq_lens, const int32_t* h_qsl,
@@ -148,9 +157,13 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.query_start_loc = mixed ? qsl : nullptr;
   a.num_seqs = num_seqs;
   a.scale = scale;
-  a.ws_acc = static_cast<float*>(workspace);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_acc = ws ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;
   a.ws_ml = a.ws_acc ? a.ws_acc + (size_t)plan.decode_units * num_q_heads * c.head_size : nullptr;
   a.decode_units = plan.decode_units;
+  a.full_units = plan.full_units;
+  a.class_start[0] = 0;
+  for (int k = 0; k < pkv::kPartClasses; ++k) a.class_start[k + 1] = a.class_start[k] + plan.class_count[k];
   a.prefill_tiles = plan.prefill_tiles;
   a.prefill_seqs = plan.prefill_seqs;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -14,6 +14,10 @@ constexpr int kPartTokens = 256;
 // Query positions per prefill workgroup: its 4 waves of 32 query rows cover
 // the G query heads of one kv head, so 128 / G positions.
 constexpr int prefill_tile_q(int g) { return 128 / g; }
+// Size classes of the short last partitions (by 32-token steps).
+constexpr int kPartClasses = kPartTokens / 32;
+// Bytes at the start of the attention workspace before the partials.
+constexpr size_t kWorkspaceHeader = 256;
 
 struct CacheDesc {
   char* kv;
@@ -37,6 +41,8 @@ struct AttnDesc {
   float* ws_acc;                   // [units][hq][D]
   float* ws_ml;                    // [units][hq][2]
   int64_t decode_units;            // split-K work units over all decode rows
+  int64_t full_units;              // of which full kPartTokens partitions
+  int64_t class_start[kPartClasses + 1];  // partial units before size class k
   int64_t prefill_tiles;           // prefill q-tiles over all prefill rows
   int prefill_seqs;                // sequences with more than one query row
 };

@@ -151,37 +151,67 @@ hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t n
 }
 
 // ---------------------------------------------------------------------------
-// Decode work units.  A unit is one 256-token partition of one decode row;
-// units are numbered sequence by sequence.  A wave finds its unit's sequence
-// with a scan over the lengths (cheap next to the 128 KiB it then reads).
+// Decode work units.  A unit is one partition of one decode row: a full
+// 256-token partition, or the shorter last partition of a row.  All full
+// units come first (sequence by sequence), then the partial ones from the
+// longest size class to the shortest, so the short work lands at the end of
+// the grid and evens out the tail.  A wave finds its unit's sequence with a
+// scan over the lengths.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int decode_parts(const int32_t* seq_lens, const int32_t* qsl, int s) {
-  const int L = seq_lens[s];
+__device__ __forceinline__ int row_len(const int32_t* seq_lens, const int32_t* qsl, int s) {
   const int ql = qsl ? qsl[s + 1] - qsl[s] : 1;
-  return (ql == 1 && L > 0) ? (L + kPartTokens - 1) / kPartTokens : 0;
+  return ql == 1 ? seq_lens[s] : 0;  // only single-query rows are decode rows
 }
+struct FullUnits {
+  __device__ int operator()(int L) const { return L > 0 ? L / kPartTokens : 0; }
+};
+// The short last partitions are numbered by size class: class k holds the
+// rows whose last partition takes 8 - k steps of 32 tokens, so larger ones
+// are handed out first.
+__device__ __forceinline__ int partial_class(int L) {
+  const int rem = L % kPartTokens;
+  return rem ? kPartTokens / 32 - (rem + 31) / 32 : -1;
+}
+struct PartialClass {
+  int k;
+  __device__ int operator()(int L) const { return (L > 0 && partial_class(L) == k) ? 1 : 0; }
+};
 
-// Sum over sequences [0, s_end) of decode_parts; every lane gets it.
-__device__ int parts_before(const int32_t* seq_lens, const int32_t* qsl, int s_end) {
+// Sum over sequences [0, s_end) of count(row length); every lane gets it.
+template <typename F>
+__device__ int units_before(const int32_t* seq_lens, const int32_t* qsl, int s_end, F count) {
   const int lane = threadIdx.x & 63;
   int acc = 0;
-  for (int s0 = 0; s0 < s_end; s0 += 64) {
-    const int s = s0 + lane;
-    int n = (s < s_end) ? decode_parts(seq_lens, qsl, s) : 0;
-    acc += n;
+  for (int s0 = 0; s0 < s_end; s0 += 256) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + 4 * lane + k;
+      acc += (s < s_end) ? count(row_len(seq_lens, qsl, s)) : 0;
+    }
   }
   return (int)wave_sum((float)acc);  // exact: counts stay far below 2^24
 }
 
-// Find (sequence, partition, partitions of that sequence) of unit u.
-__device__ bool find_unit(int u, const int32_t* seq_lens, const int32_t* qsl, int num_seqs,
-                          int& s_out, int& part_out, int& nparts_out) {
+// Find the sequence holding item u when sequence s has count(L_s) items,
+// and u's index among them.  Each lane counts 4 consecutive sequences, so
+// 256 lengths are read with four independent loads per lane before one wave
+// scan.  Returns the sequence's length in len_out.
+template <typename F>
+__device__ bool find_unit(int u, const int32_t* seq_lens, const int32_t* qsl, int num_seqs, F count,
+                          int& s_out, int& idx_out, int& len_out) {
   const int lane = threadIdx.x & 63;
   int base = 0;
-  for (int s0 = 0; s0 < num_seqs; s0 += 64) {
-    const int s = s0 + lane;
-    const int n = (s < num_seqs) ? decode_parts(seq_lens, qsl, s) : 0;
-    int incl = n;
+  for (int s0 = 0; s0 < num_seqs; s0 += 256) {
+    int n[4], len[4];
+    int tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + 4 * lane + k;
+      len[k] = (s < num_seqs) ? row_len(seq_lens, qsl, s) : 0;
+      n[k] = count(len[k]);
+      tot += n[k];
+    }
+    int incl = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int t = __shfl_up(incl, off);
@@ -190,12 +220,23 @@ __device__ bool find_unit(int u, const int32_t* seq_lens, const int32_t* qsl, in
     const int total = __shfl(incl, 63);
     if (u < base + total) {
       const unsigned long long m = __ballot(base + incl > u);
-      const int ls = __ffsll((unsigned long long)m) - 1;
-      const int incl_s = __shfl(incl, ls);
-      const int n_s = __shfl(n, ls);
-      s_out = uniform(s0 + ls);
-      part_out = uniform(u - (base + incl_s - n_s));
-      nparts_out = uniform(n_s);
+      const int hit = __ffsll((unsigned long long)m) - 1;
+      // inside the lane that holds u: the first of its 4 sequences whose
+      // range ends past u
+      const int run = base + incl - tot;
+      int kk = 3, before = run, start = run;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (kk == 3 && u < start + n[k]) { kk = k; before = start; }
+        start += n[k];
+      }
+      if (!(u < before + n[kk])) before = run + n[0] + n[1] + n[2];
+      int lk = len[0];
+#pragma unroll
+      for (int k = 1; k < 4; ++k) lk = (kk == k) ? len[k] : lk;
+      s_out = uniform(__shfl(s0 + 4 * lane + kk, hit));
+      idx_out = uniform(__shfl(u - before, hit));
+      len_out = uniform(__shfl(lk, hit));
       return true;
     }
     base += total;
@@ -229,6 +270,9 @@ struct DecodeParams {
   float scale_log2;
   float* ws_acc;
   float* ws_ml;
+  int full_units;   // units [0, full_units) are full partitions
+  int total_items;  // units * kv heads
+  int class_start[kPartClasses + 1];  // partial units before size class k
 };
 
 template <int ES, int D, int G, bool CHECK>
@@ -236,20 +280,30 @@ __device__ __forceinline__ void pv_block(const uint4 (&vr)[BS * D * ES / 16 / 64
                                          const float* __restrict__ p_lds, int key_base,
                                          int valid_keys, float (&acc)[G][D / 64]) {
   constexpr int E = 16 / ES;
-  constexpr int VG = BS * D * ES / 16 / 64;
+  constexpr int DPL = D / 64;
+  // load i covers key granule i / DPL and the lane's d value i % DPL
 #pragma unroll
-  for (int i = 0; i < VG; ++i) {
-    const int kg = (i * 64) / D;         // key granule of this load
-    const int dd = ((i * 64) % D) / 64;  // which of the lane's d values
+  for (int kg = 0; kg < BS / E; ++kg) {
+    float pk[E][G];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int key = kg * E + e;
-      if (CHECK && key >= valid_keys) continue;
-      const float v = granule_elem<ES>(vr[i], e);
-      const float* pp = p_lds + (key_base + key) * G;
+    for (int e = 0; e < E; ++e)
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(pp[g], v, acc[g][dd]);
+      for (int g = 0; g < G; ++g) pk[e][g] = p_lds[(key_base + kg * E + e) * G + g];
+#pragma unroll
+    for (int dd = 0; dd < DPL; ++dd) {
+      const uint4 w = vr[kg * DPL + dd];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (CHECK && kg * E + e >= valid_keys) continue;
+        const float v = granule_elem<ES>(w, e);
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(pk[e][g], v, acc[g][dd]);
+      }
     }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int dd = 0; dd < DPL; ++dd) asm volatile("" : "+v"(acc[g][dd]));
   }
 }
 
@@ -270,6 +324,15 @@ struct StepRegs {
   uint4 v[2][DecodeShape<ES, D>::VG];
 };
 
+// Per-item state of a decode wave: which unit of which row, and where.
+struct DecodeItem {
+  int valid;
+  int s, part, L, row, kvh, unit;
+  int tok0, tok_end, nsteps, nparts;
+  int my_id;  // lane i < number of blocks of the unit: its i-th physical block
+  int buf;    // which LDS q buffer holds this item's query rows
+};
+
 template <int ES, int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_partition(
     DecodeParams p) {
@@ -277,50 +340,65 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   static_assert(D % 64 == 0, "head size must be a multiple of 64");
   static_assert(kPartTokens % 32 == 0 && kPartTokens / BS <= 64, "partition size");
 
-  // q rows of the group, each half row padded by 16 bytes so the two halves
-  // read in one instruction fall in different banks.
-  __shared__ __align__(16) char q_lds[G * 2 * S::QROW];
+  // Two q buffers (current and next item), each half row padded by 16 bytes
+  // so the two halves read in one instruction fall in different banks.
+  __shared__ __align__(16) char q_lds[2][G * 2 * S::QROW];
   __shared__ __align__(16) float p_lds[32 * G];
 
   const int lane = threadIdx.x;
-  const int kvh = blockIdx.x % p.hkv;
-  const int unit = blockIdx.x / p.hkv;
-  int s, part, nparts;
-  if (!find_unit(unit, p.seq_lens, p.qsl, p.num_seqs, s, part, nparts)) return;
-
-  const int L = p.seq_lens[s];
-  const int row = p.qsl ? p.qsl[s] : s;
   const int hq = p.hkv * G;
-
-  {
-    constexpr int QGR = G * S::KG;  // 16-byte granules of the group's q rows
-    const uint4* src = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(p.q) + ((size_t)row * hq + (size_t)kvh * G) * D * ES);
-    for (int i = lane; i < QGR; i += 64) {
-      const int g = i / S::KG, c = i % S::KG;
-      const int half = c / S::KH, cc = c % S::KH;
-      *reinterpret_cast<uint4*>(q_lds + (g * 2 + half) * S::QROW + cc * 16) = src[i];
-    }
-  }
-
-  const int tok0 = part * kPartTokens;
-  const int tok_end = min(L, tok0 + kPartTokens);
-  const int nblk = (tok_end - tok0 + BS - 1) / BS;
-  const int nsteps = (nblk + 1) / 2;
-  // lane i < nblk holds the partition's i-th physical block id; later lanes
-  // repeat the last one so over-reads stay inside valid blocks.
-  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks + tok0 / BS;
-  const int my_id = bt[min(lane, nblk - 1)];
-  const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
-
   const int half = lane & 1;           // which half of the K row
   const int t_in_blk = (lane >> 1) & 15;
   const int bsel = lane >> 5;          // which block of the step
   const int k_lane_off = (half * S::KH * BS + t_in_blk) * 16;
 
-  auto load = [&](StepRegs<ES, D>& r, int st) {
-    const int b0 = uniform(__builtin_amdgcn_readlane(my_id, 2 * st));
-    const int b1 = uniform(__builtin_amdgcn_readlane(my_id, 2 * st + 1));
+  // Work item i = unit * hkv + kv head; this wave takes items
+  // blockIdx.x, blockIdx.x + gridDim.x, ...  Units run full partitions first,
+  // so the short last partitions fall at the end of every wave's list.
+  auto setup = [&](DecodeItem& it, int item, int buf) {
+    it.valid = item < p.total_items;
+    if (!it.valid) return;
+    it.kvh = item % p.hkv;
+    it.unit = item / p.hkv;
+    it.buf = buf;
+    int s, part, L;
+    if (it.unit < p.full_units) {
+      find_unit(it.unit, p.seq_lens, p.qsl, p.num_seqs, FullUnits(), s, part, L);
+    } else {
+      const int v = it.unit - p.full_units;
+      int k = 0;
+#pragma unroll
+      for (int c = 1; c < kPartClasses; ++c) k += v >= p.class_start[c] ? 1 : 0;
+      find_unit(v - p.class_start[k], p.seq_lens, p.qsl, p.num_seqs, PartialClass{k}, s, part, L);
+      part = L / kPartTokens;  // the last, partial partition of the row
+    }
+    it.s = s;
+    it.part = part;
+    it.L = L;
+    it.nparts = (L + kPartTokens - 1) / kPartTokens;
+    it.row = p.qsl ? p.qsl[s] : s;
+    it.tok0 = part * kPartTokens;
+    it.tok_end = min(L, it.tok0 + kPartTokens);
+    const int nblk = (it.tok_end - it.tok0 + BS - 1) / BS;
+    it.nsteps = (nblk + 1) / 2;
+    // lane i < nblk holds the unit's i-th physical block id; later lanes
+    // repeat the last one so over-reads stay inside valid blocks.
+    const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks + it.tok0 / BS;
+    it.my_id = bt[min(lane, nblk - 1)];
+    constexpr int QGR = G * S::KG;  // 16-byte granules of the group's q rows
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + ((size_t)it.row * hq + (size_t)it.kvh * G) * D * ES);
+    for (int i = lane; i < QGR; i += 64) {
+      const int g = i / S::KG, c = i % S::KG;
+      const int hh = c / S::KH, cc = c % S::KH;
+      *reinterpret_cast<uint4*>(q_lds[buf] + (g * 2 + hh) * S::QROW + cc * 16) = src[i];
+    }
+  };
+
+  auto load = [&](StepRegs<ES, D>& r, const DecodeItem& it, int st) {
+    const int b0 = uniform(__builtin_amdgcn_readlane(it.my_id, 2 * st));
+    const int b1 = uniform(__builtin_amdgcn_readlane(it.my_id, 2 * st + 1));
+    const char* head_base = p.kv + (size_t)it.kvh * 2 * S::TILE;
     const char* base0 = head_base + (size_t)b0 * p.block_bytes;
     const char* base1 = head_base + (size_t)b1 * p.block_bytes;
     const char* kp = (bsel ? base1 : base0) + k_lane_off;
@@ -334,21 +412,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   };
 
   float m_run[G], l_lane[G], acc[G][S::DPL];
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_lane[g] = 0.f;
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_lane[g] = 0.f;
 #pragma unroll
-    for (int j = 0; j < S::DPL; ++j) acc[g][j] = 0.f;
-  }
+      for (int j = 0; j < S::DPL; ++j) acc[g][j] = 0.f;
+    }
+  };
 
-  auto compute = [&](const StepRegs<ES, D>& r, int st) {
-    // ---- scores: q granules are read from LDS one step ahead of use; the
-    // compiler barrier keeps the scheduler from hoisting all of them.
+  auto compute = [&](const StepRegs<ES, D>& r, const DecodeItem& it, int st) {
+    // ---- scores: q granules are read from LDS one step ahead of use
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
-    const char* qh = q_lds + half * S::QROW;
+    const char* qh = q_lds[it.buf] + half * S::QROW;
     uint4 qcur[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) qcur[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW);
@@ -380,13 +459,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         }
         qcur[g] = qnext[g];
       }
-      asm volatile("" ::: "memory");
+      // Pin the partial sums here so the compiler cannot sink whole
+      // dot products (keeping every q granule live) past this point.
+#pragma unroll
+      for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
     }
 
     // ---- online softmax (log2 domain); the pair of lanes of a token
     // completes its dot product with one swap-add.
-    const int tok = tok0 + st * 32 + (lane >> 1);
-    const bool tok_ok = tok < tok_end;
+    const int tok = it.tok0 + st * 32 + (lane >> 1);
+    const bool tok_ok = tok < it.tok_end;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float full = sc[g] + dpp_f<0xB1>(sc[g]);
@@ -410,63 +492,77 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     // ---- weighted V
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int valid = tok_end - (tok0 + (2 * st + j) * BS);
+      const int valid = it.tok_end - (it.tok0 + (2 * st + j) * BS);
       if (valid >= BS)
         pv_block<ES, D, G, false>(r.v[j], p_lds, j * BS, BS, acc);
       else if (valid > 0)
         pv_block<ES, D, G, true>(r.v[j], p_lds, j * BS, valid, acc);
-      asm volatile("" ::: "memory");
     }
     __syncthreads();
   };
 
-  __syncthreads();  // q rows visible
-  StepRegs<ES, D> ra, rb;
-  load(ra, 0);
-  for (int st = 0; st < nsteps; st += 2) {
-    if (st + 1 < nsteps) load(rb, st + 1);
-    compute(ra, st);
-    if (st + 1 < nsteps) {
-      if (st + 2 < nsteps) load(ra, st + 2);
-      compute(rb, st + 1);
-    }
-  }
-
-  float l_tot[G];
+  auto finish = [&](const DecodeItem& it) {
+    float l_tot[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_lane[g]);
-
-  if (nparts == 1) {
-    float* o = p.out + ((size_t)row * hq + (size_t)kvh * G) * D;
+    for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_lane[g]);
+    if (it.nparts == 1) {
+      float* o = p.out + ((size_t)it.row * hq + (size_t)it.kvh * G) * D;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int j = 0; j < S::DPL; ++j) o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g];
-    }
-  } else {
-    const size_t w = (size_t)unit * hq + (size_t)kvh * G;
+        for (int j = 0; j < S::DPL; ++j) o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g];
+      }
+    } else {
+      const size_t w = (size_t)it.unit * hq + (size_t)it.kvh * G;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int j = 0; j < S::DPL; ++j) p.ws_acc[(w + g) * D + j * 64 + lane] = acc[g][j];
-      if (lane == 0) {
-        p.ws_ml[(w + g) * 2] = m_run[g];
-        p.ws_ml[(w + g) * 2 + 1] = l_tot[g];
+        for (int j = 0; j < S::DPL; ++j) p.ws_acc[(w + g) * D + j * 64 + lane] = acc[g][j];
+        if (lane == 0) {
+          p.ws_ml[(w + g) * 2] = m_run[g];
+          p.ws_ml[(w + g) * 2 + 1] = l_tot[g];
+        }
       }
     }
+    reset_state();
+  };
+
+  // The unit's steps, two register sets alternating: the loads of step
+  // st + 1 are in flight while step st is computed.
+  DecodeItem cur;
+  setup(cur, blockIdx.x, 0);
+  if (!cur.valid) return;
+  reset_state();
+  __syncthreads();  // q rows visible
+  StepRegs<ES, D> ra, rb;
+  load(ra, cur, 0);
+  for (int st = 0; st < cur.nsteps; st += 2) {
+    if (st + 1 < cur.nsteps) load(rb, cur, st + 1);
+    compute(ra, cur, st);
+    if (st + 1 < cur.nsteps) {
+      if (st + 2 < cur.nsteps) load(ra, cur, st + 2);
+      compute(rb, cur, st + 1);
+    }
   }
+  finish(cur);
 }
 
 // ---------------------------------------------------------------------------
 // Merge pass for decode rows split over several partitions:
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// One wave per (sequence, kv head); also writes the zero row of an empty
-// sequence.
+// One workgroup per (sequence, kv head), one wave per query head of the
+// group.  Lane p holds partition p's (m, l), so the max, the weights and the
+// denominator are wave reductions; the weighted sum over partitions then
+// runs with lanes over d and eight partitions' loads in flight at a time.
+// Also writes the zero row of an empty sequence.
 // ---------------------------------------------------------------------------
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p) {
+__global__ __launch_bounds__(256) void k_decode_merge(DecodeParams p) {
   constexpr int DPL = D / 64;
-  const int lane = threadIdx.x;
+  constexpr int NW = G < 4 ? G : 4;  // waves per workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (wave >= NW) return;
   const int kvh = blockIdx.x % p.hkv;
   const int s = blockIdx.x / p.hkv;
   const int ql = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
@@ -474,42 +570,83 @@ __global__ __launch_bounds__(64) void k_decode_merge(DecodeParams p) {
   const int L = p.seq_lens[s];
   const int row = p.qsl ? p.qsl[s] : s;
   const int hq = p.hkv * G;
-  float* o = p.out + ((size_t)row * hq + (size_t)kvh * G) * D;
   if (L <= 0) {
-    for (int i = lane; i < G * D; i += 64) o[i] = 0.f;
+    for (int g = wave; g < G; g += NW) {
+      float* o = p.out + ((size_t)row * hq + (size_t)kvh * G + g) * D;
+      for (int i = lane; i < D; i += 64) o[i] = 0.f;
+    }
     return;
   }
   const int nparts = (L + kPartTokens - 1) / kPartTokens;
   if (nparts == 1) return;
-  const int u0 = parts_before(p.seq_lens, p.qsl, s);
-  for (int g = 0; g < G; ++g) {
+  // partition q < nfull is unit u_full + q; a partial last one is unit u_part
+  const int nfull = L / kPartTokens;
+  const int u_full = units_before(p.seq_lens, p.qsl, s, FullUnits());
+  const int kc = partial_class(L);
+  const int u_part =
+      kc < 0 ? 0 : p.full_units + p.class_start[kc] + units_before(p.seq_lens, p.qsl, s, PartialClass{kc});
+  auto unit_of = [&](int q) { return q < nfull ? u_full + q : u_part; };
+  for (int g = wave; g < G; g += NW) {
+    const size_t gh = (size_t)kvh * G + g;
     float M = -INFINITY;
-    for (int q = 0; q < nparts; ++q) M = fmaxf(M, p.ws_ml[(((size_t)(u0 + q)) * hq + kvh * G + g) * 2]);
+    for (int c = 0; c < nparts; c += 64) {
+      const int q = c + lane;
+      if (q < nparts) M = fmaxf(M, p.ws_ml[((size_t)unit_of(q) * hq + gh) * 2]);
+    }
+    M = wave_max(M);
     float den = 0.f;
     float num[DPL];
 #pragma unroll
     for (int j = 0; j < DPL; ++j) num[j] = 0.f;
-    for (int q = 0; q < nparts; ++q) {
-      const size_t w = ((size_t)(u0 + q)) * hq + (size_t)kvh * G + g;
-      const float sc = __builtin_amdgcn_exp2f(p.ws_ml[w * 2] - M);
-      den = fmaf(sc, p.ws_ml[w * 2 + 1], den);
+    for (int c = 0; c < nparts; c += 64) {
+      const int q = c + lane;
+      float wq = 0.f;
+      if (q < nparts) {
+        const size_t wi = (size_t)unit_of(q) * hq + gh;
+        wq = __builtin_amdgcn_exp2f(p.ws_ml[wi * 2] - M);
+        den = fmaf(wq, p.ws_ml[wi * 2 + 1], den);
+      }
+      const int n = min(64, nparts - c);
+      int i = 0;
+      for (; i + 8 <= n; i += 8) {
+        float a[8][DPL];
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) num[j] = fmaf(sc, p.ws_acc[w * D + j * 64 + lane], num[j]);
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int j = 0; j < DPL; ++j)
+            a[k][j] = p.ws_acc[((size_t)unit_of(c + i + k) * hq + gh) * D + j * 64 + lane];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), i + k));
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) num[j] = fmaf(wk, a[k][j], num[j]);
+        }
+      }
+      for (; i < n; ++i) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), i));
+#pragma unroll
+        for (int j = 0; j < DPL; ++j)
+          num[j] = fmaf(wk, p.ws_acc[((size_t)unit_of(c + i) * hq + gh) * D + j * 64 + lane], num[j]);
+      }
     }
+    den = wave_sum(den);
+    float* o = p.out + ((size_t)row * hq + (size_t)kvh * G + g) * D;
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+    for (int j = 0; j < DPL; ++j) o[j * 64 + lane] = num[j] / den;
   }
 }
 
 template <int ES, int D, int G>
 static hipError_t decode_rows_t(const DecodeParams& p, int64_t units, int num_seqs, int hkv,
                                 hipStream_t stream) {
-  if (units > 0)
-    hipLaunchKernelGGL((k_decode_partition<ES, D, G>), dim3((unsigned)(units * hkv)), dim3(64), 0,
-                       stream, p);
+  if (units > 0) {
+    const int64_t items = units * hkv;
+    hipLaunchKernelGGL((k_decode_partition<ES, D, G>), dim3((unsigned)items), dim3(64), 0, stream,
+                       p);
+  }
   if (num_seqs > 0)
-    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((int64_t)num_seqs * hkv)), dim3(64),
-                       0, stream, p);
+    hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((int64_t)num_seqs * hkv)),
+                       dim3(64 * (G < 4 ? G : 4)), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -542,6 +679,9 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
   p.scale_log2 = a.scale * kLog2e;
   p.ws_acc = a.ws_acc;
   p.ws_ml = a.ws_ml;
+  p.full_units = (int)a.full_units;
+  p.total_items = (int)(a.decode_units * c.hkv);
+  for (int k = 0; k <= kPartClasses; ++k) p.class_start[k] = (int)a.class_start[k];
   const int G = a.hq / c.hkv;
   if (c.dtype_bytes == 4) {
     if (c.head_size == 64) return decode_rows_g<4, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);

@@ -163,3 +163,23 @@ def test_split_boundaries():
     assert np.array_equal(st.pool_codes(), ref["pool"])
     _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", "split boundaries")
     del w
+
+
+def test_many_sequences_and_long_rows():
+    """More sequences than one 256-wide length scan covers, and rows longer
+    than 64 partitions."""
+    rng = np.random.default_rng(11)
+    B = 600
+    L = rng.integers(1, 600, size=B, endpoint=True).astype(np.int32)
+    L[7] = 20000                                    # 79 partitions of 256
+    streams = [np.random.default_rng(x) for x in (21, 22, 23, 24)]
+    pool = int(1.25 * sum((int(x) + 15) // 16 for x in L)) + 1
+    w = workloads._build(3, "many seqs", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                         np.ones(B, np.int32), pool, streams)
+    _announce(f"many sequences B={B}, longest {int(L.max())}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    rows = [0, 7, 255, 256, 257, 511, 512, 599]
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in rows])
+    got = np.concatenate([out[s:s + 1] for s in rows])
+    _check_attention(got, want, "bf16", "many sequences")

@@ -157,9 +157,12 @@ def test_workspace_sizing():
     cache.desc = d
     lens = np.array([1, 256, 257, 0, 8192], np.int32)
     units = 1 + 1 + 2 + 0 + 32
-    assert P.pkv_attention_workspace_bytes(cache, 32, lens) == units * 32 * (128 + 2) * 4
+    header = 256                                      # workspace header
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens) == header + units * 32 * (128 + 2) * 4
     qsl = np.array([0, 1, 2, 3, 3, 1000], np.int32)   # seq 4 is a prefill chunk
-    assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == 4 * 32 * 130 * 4
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == header + 4 * 32 * 130 * 4
+    only_prefill = np.array([0, 1000], np.int32)
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens[4:], only_prefill) == 0
 
 
 def _call_decode(cache_desc, out=1, q=1, bt=1, sl=1, h_sl=None, n=1, hq=32, ws=None, ws_bytes=0,
