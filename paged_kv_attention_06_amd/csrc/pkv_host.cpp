@@ -167,9 +167,9 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.prefill_tiles = plan.prefill_tiles;
   a.prefill_seqs = plan.prefill_seqs;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (plan.prefill_tiles > 0) {
-    if (int e = hip_status(pkv::launch_prefill_rows(c, a, st), "prefill rows")) return e;
-  }
+  if (plan.prefill_tiles > 0 && plan.decode_units > 0)
+    return hip_status(pkv::launch_mixed_rows(c, a, st), "mixed rows");
+  if (plan.prefill_tiles > 0) return hip_status(pkv::launch_prefill_rows(c, a, st), "prefill rows");
   return hip_status(pkv::launch_decode_rows(c, a, st), "decode rows");
 }
 

@@ -54,8 +54,11 @@ hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t n
 // Decode rows (one query row per sequence, or the q_len == 1 rows of a mixed
 // batch): split-K partition pass, then the merge of multi-partition rows.
 hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
-// Prefill rows of a mixed batch (q_len > 1): MFMA tiles.
+// Prefill rows of a mixed batch (q_len > 1) when it has no decode rows: MFMA tiles.
 hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
+// A batch with both kinds of rows: one launch in which prefill tiles and
+// decode units share the GPU, then the merge of split decode rows.
+hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 
 bool supported_group(int g);
 // Group sizes the mixed path's prefill rows support (bf16 caches only).

@@ -71,6 +71,16 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Orders one wave's LDS writes before its later LDS reads by other lanes.
+// A wave's LDS operations execute in issue order, so keeping the compiler
+// from moving accesses across this point is enough; waves of a workgroup
+// that work independently need no workgroup barrier.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // ---------------------------------------------------------------------------
 // KV write: one thread per (token, kv head, 16-byte granule of the row).
 // ---------------------------------------------------------------------------
@@ -333,19 +343,27 @@ struct DecodeItem {
   int buf;    // which LDS q buffer holds this item's query rows
 };
 
+// LDS of one decode wave: two q buffers (each half row padded by 16 bytes so
+// the two halves read in one instruction fall in different banks) and the
+// probabilities of one step.
 template <int ES, int D, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_partition(
-    DecodeParams p) {
+struct DecodeLds {
+  static constexpr int QBUF = G * 2 * DecodeShape<ES, D>::QROW;
+  static constexpr int BYTES = 2 * QBUF + 32 * G * 4;
+};
+
+// One decode work item (unit, kv head) on one wave; `lds` is the wave's own
+// DecodeLds area.  Waves are independent: only wave-level ordering is used.
+template <int ES, int D, int G>
+__device__ __forceinline__ void decode_item(const DecodeParams& p, int item, char* lds) {
   using S = DecodeShape<ES, D>;
   static_assert(D % 64 == 0, "head size must be a multiple of 64");
   static_assert(kPartTokens % 32 == 0 && kPartTokens / BS <= 64, "partition size");
+  constexpr int QBUF = DecodeLds<ES, D, G>::QBUF;
+  auto q_lds = [lds](int b) { return lds + b * QBUF; };
+  float* p_lds = reinterpret_cast<float*>(lds + 2 * QBUF);
 
-  // Two q buffers (current and next item), each half row padded by 16 bytes
-  // so the two halves read in one instruction fall in different banks.
-  __shared__ __align__(16) char q_lds[2][G * 2 * S::QROW];
-  __shared__ __align__(16) float p_lds[32 * G];
-
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int hq = p.hkv * G;
   const int half = lane & 1;           // which half of the K row
   const int t_in_blk = (lane >> 1) & 15;
@@ -391,7 +409,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int i = lane; i < QGR; i += 64) {
       const int g = i / S::KG, c = i % S::KG;
       const int hh = c / S::KH, cc = c % S::KH;
-      *reinterpret_cast<uint4*>(q_lds[buf] + (g * 2 + hh) * S::QROW + cc * 16) = src[i];
+      *reinterpret_cast<uint4*>(q_lds(buf) + (g * 2 + hh) * S::QROW + cc * 16) = src[i];
     }
   };
 
@@ -427,7 +445,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
-    const char* qh = q_lds[it.buf] + half * S::QROW;
+    const char* qh = q_lds(it.buf) + half * S::QROW;
     uint4 qcur[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) qcur[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW);
@@ -487,7 +505,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
         p_lds[(lane >> 1) * G + g] = pr;
       }
     }
-    __syncthreads();
+    wave_sync();
 
     // ---- weighted V
 #pragma unroll
@@ -498,7 +516,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       else if (valid > 0)
         pv_block<ES, D, G, true>(r.v[j], p_lds, j * BS, valid, acc);
     }
-    __syncthreads();
+    wave_sync();
   };
 
   auto finish = [&](const DecodeItem& it) {
@@ -530,10 +548,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   // The unit's steps, two register sets alternating: the loads of step
   // st + 1 are in flight while step st is computed.
   DecodeItem cur;
-  setup(cur, blockIdx.x, 0);
+  setup(cur, item, 0);
   if (!cur.valid) return;
   reset_state();
-  __syncthreads();  // q rows visible
+  wave_sync();  // q rows visible
   StepRegs<ES, D> ra, rb;
   load(ra, cur, 0);
   for (int st = 0; st < cur.nsteps; st += 2) {
@@ -545,6 +563,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   }
   finish(cur);
+}
+
+template <int ES, int D, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_partition(
+    DecodeParams p) {
+  __shared__ __align__(16) char lds[DecodeLds<ES, D, G>::BYTES];
+  decode_item<ES, D, G>(p, blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -664,7 +689,7 @@ static hipError_t decode_rows_g(int G, const DecodeParams& p, int64_t units, int
 
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
-hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+static DecodeParams make_decode_params(const CacheDesc& c, const AttnDesc& a) {
   DecodeParams p;
   p.kv = c.kv;
   p.block_bytes = c.block_bytes;
@@ -682,6 +707,11 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
   p.full_units = (int)a.full_units;
   p.total_items = (int)(a.decode_units * c.hkv);
   for (int k = 0; k <= kPartClasses; ++k) p.class_start[k] = (int)a.class_start[k];
+  return p;
+}
+
+hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  const DecodeParams p = make_decode_params(c, a);
   const int G = a.hq / c.hkv;
   if (c.dtype_bytes == 4) {
     if (c.head_size == 64) return decode_rows_g<4, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);
@@ -774,17 +804,27 @@ __device__ __forceinline__ uint32_t pack_hi(float a, float b) {
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void k_prefill_tile(PrefillParams p) {
+struct PrefillLds {
+  static constexpr int BYTES = PrefillShape<D, G>::KT * PrefillShape<D, G>::KROW +
+                               D * PrefillShape<D, G>::VROW;
+};
+
+// One prefill work item (q tile, kv head) on a whole 4-wave workgroup; `lds`
+// holds the K tile then the V^T tile.
+template <int D, int G>
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds) {
   using S = PrefillShape<D, G>;
   static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
-  __shared__ __align__(16) char k_lds[S::KT * S::KROW];
-  __shared__ __align__(16) char v_lds[D * S::VROW];
+  constexpr int KGR = 2 * D;           // 16-byte granules per K (or V) tile of one block
+  constexpr int NG = 4 * KGR / 256;    // granules of K (and of V) per thread per LDS tile
+  char* k_lds = lds;
+  char* v_lds = lds + S::KT * S::KROW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kvh = blockIdx.x % p.hkv;
-  const int item = blockIdx.x / p.hkv;
+  const int kvh = work % p.hkv;
+  const int item = work / p.hkv;
   int s, tile, ntiles;
   const int32_t* qsl = p.qsl;
   auto tiles_of = [qsl](int q) {
@@ -836,75 +876,74 @@ __global__ __launch_bounds__(256) void k_prefill_tile(PrefillParams p) {
   const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
   const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * S::KT;
-    __syncthreads();  // the previous tile is consumed
-    // ---- gather 4 blocks' K and V through the block table into LDS
-    constexpr int KGR = 2 * D;  // 16-byte granules per K (or V) tile
+  // ---- K/V of one 64-key tile: global -> registers (issued a tile ahead),
+  // then registers -> LDS.  Keys at or past L (never written) are zeroed in
+  // V, since 0 * NaN would poison the MFMA sums; K there is masked instead.
+  uint4 kst[NG], vst[NG];
+  auto gload = [&](int kt) {
 #pragma unroll
-    for (int gi = tid; gi < 4 * KGR; gi += 256) {
+    for (int i = 0; i < NG; ++i) {
+      const int gi = tid + 256 * i;
       const int bl = gi / KGR;
       const int blk = kt * 4 + bl;
-      const bool valid = blk * BS < kend;
       const int within = gi % KGR;
-      if (valid) {
-        const int phys = bt[blk];
-        const char* base = head_base + (size_t)phys * p.block_bytes;
-        {  // K granule (c, t): 8 consecutive d of token t
-          const int c = within / BS, t = within % BS;
-          const uint4 v = *reinterpret_cast<const uint4*>(base + (c * BS + t) * 16);
-          *reinterpret_cast<uint4*>(k_lds + (bl * BS + t) * S::KROW + c * 16) = v;
-        }
-        {  // V granule (kg, d): 8 consecutive keys of one d
-          const int kg = within / D, d = within % D;
-          uint4 v = *reinterpret_cast<const uint4*>(base + S::TILE + (kg * D + d) * 16);
-          const int key0 = blk * BS + kg * 8;
-          if (key0 + 8 > L) {  // keys at or past L were never written: zero them
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            v = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-          *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) = v;
-        }
-      } else {
+      kst[i] = make_uint4(0, 0, 0, 0);
+      vst[i] = make_uint4(0, 0, 0, 0);
+      if (blk * BS < kend) {
+        const char* base = head_base + (size_t)bt[blk] * p.block_bytes;
+        const int c = within / BS, t = within % BS;
+        kst[i] = *reinterpret_cast<const uint4*>(base + (c * BS + t) * 16);
         const int kg = within / D, d = within % D;
-        *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) =
-            make_uint4(0, 0, 0, 0);
+        uint4 v = *reinterpret_cast<const uint4*>(base + S::TILE + (kg * D + d) * 16);
+        const int key0 = blk * BS + kg * 8;
+        if (key0 + 8 > L) {
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        vst[i] = v;
       }
     }
-    __syncthreads();
-    if (k0 > wlast) continue;  // every key of the tile is after this wave's rows
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int gi = tid + 256 * i;
+      const int bl = gi / KGR;
+      const int within = gi % KGR;
+      const int c = within / BS, t = within % BS;
+      *reinterpret_cast<uint4*>(k_lds + (bl * BS + t) * S::KROW + c * 16) = kst[i];
+      const int kg = within / D, d = within % D;
+      *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) = vst[i];
+    }
+  };
 
-    // ---- S^T for two 32-key sub-tiles
-    f32x16_t sacc[2];
-    float x[2][16];
+  // ---- one 32-key chunk: scores S^T (MFMA), online softmax, P split into
+  // bf16 hi + lo, O^T += V^T P^T (MFMA).
+  auto scores = [&](int j, f32x16_t& sacc) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    const char* krow = k_lds + (32 * j + r) * S::KROW + h * 16;
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const uint4 a = *reinterpret_cast<const uint4*>(krow + ks * 32);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], sacc,
+                                                     0, 0, 0);
+    }
+  };
+  auto softmax_pv = [&](int k0, int j, const f32x16_t& sacc) {
+    const int kj = k0 + 32 * j;
+    float x[16];
     float mt = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kj = k0 + 32 * j;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[j][i] = 0.f;
-      if (kj <= wlast) {
-        const char* krow = k_lds + (32 * j + r) * S::KROW + h * 16;
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-          const uint4 a = *reinterpret_cast<const uint4*>(krow + ks * 32);
-          sacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks],
-                                                            sacc[j], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kj + 8 * (i >> 2) + 4 * h + (i & 3);
-        const bool ok = row_ok && kj <= wlast && key <= my_pos;
-        x[j][i] = ok ? sacc[j][i] * p.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[j][i]);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int key = kj + 8 * (i >> 2) + 4 * h + (i & 3);
+      x[i] = (row_ok && key <= my_pos) ? sacc[i] * p.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, x[i]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // ---- lazy rescale of this row's state
     const bool need = mt > m_run + kRescaleSlack;
     if (__ballot(need)) {
       const float corr = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
@@ -915,45 +954,61 @@ __global__ __launch_bounds__(256) void k_prefill_tile(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= corr;
     }
-    // ---- probabilities, split into bf16 hi + lo, as the B operand of PV
-    uint32_t phi[2][2][4], plo[2][2][4];
+    uint32_t phi[2][4], plo[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float a = __builtin_amdgcn_exp2f(x[j][8 * kk + 2 * m] - m_run);
-          const float b = __builtin_amdgcn_exp2f(x[j][8 * kk + 2 * m + 1] - m_run);
-          l_run += a + b;
-          const float ah = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
-          const float bh = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
-          phi[j][kk][m] = pack_hi(ah, bh);
-          plo[j][kk][m] = pack_hi(a - ah, b - bh);
-        }
+      for (int m = 0; m < 4; ++m) {
+        const float a = __builtin_amdgcn_exp2f(x[8 * kk + 2 * m] - m_run);
+        const float b = __builtin_amdgcn_exp2f(x[8 * kk + 2 * m + 1] - m_run);
+        l_run += a + b;
+        const float ah = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
+        const float bh = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
+        phi[kk][m] = pack_hi(ah, bh);
+        plo[kk][m] = pack_hi(a - ah, b - bh);
       }
     }
-    // ---- O^T += V^T P^T
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (k0 + 32 * j > wlast) continue;
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(phi[kk][0], phi[kk][1], phi[kk][2], phi[kk][3]));
+      const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(plo[kk][0], plo[kk][1], plo[kk][2], plo[kk][3]));
+      bf16x8_t a[S::DB];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t bh = __builtin_bit_cast(
-            bf16x8_t, make_uint4(phi[j][kk][0], phi[j][kk][1], phi[j][kk][2], phi[j][kk][3]));
-        const bf16x8_t bl = __builtin_bit_cast(
-            bf16x8_t, make_uint4(plo[j][kk][0], plo[j][kk][1], plo[j][kk][2], plo[j][kk][3]));
-#pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const char* vrow = v_lds + (32 * db + r) * S::VROW + (32 * j + 16 * kk + 4 * h) * 2;
-          const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16);
-          const bf16x8_t a =
-              __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, o[db], 0, 0, 0);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < S::DB; ++db) {
+        const char* vrow = v_lds + (32 * db + r) * S::VROW + (32 * j + 16 * kk + 4 * h) * 2;
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16);
+        a[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
       }
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], bh, o[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], bl, o[db], 0, 0, 0);
+    }
+  };
+
+  gload(0);
+  lstore();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * S::KT;
+    if (kt + 1 < nkt) gload(kt + 1);  // in flight while this tile is computed
+    if (k0 <= wlast) {
+      // both chunks' scores first, so the softmax of chunk 0 overlaps the
+      // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
+      const bool two = k0 + 32 <= wlast;
+      f32x16_t s0, s1;
+      scores(0, s0);
+      if (two) scores(1, s1);
+      softmax_pv(k0, 0, s0);
+      if (two) softmax_pv(k0, 1, s1);
+    }
+    __syncthreads();  // every wave is done with this tile
+    if (kt + 1 < nkt) {
+      lstore();
+      __syncthreads();
     }
   }
 
@@ -974,6 +1029,37 @@ __global__ __launch_bounds__(256) void k_prefill_tile(PrefillParams p) {
   }
 }
 
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_tile(
+    PrefillParams p) {
+  __shared__ __align__(16) char lds[PrefillLds<D, G>::BYTES];
+  prefill_item<D, G>(p, blockIdx.x, lds);
+}
+
+// One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
+// (compute-bound, MFMA) and the rest run four decode items each, one per
+// wave (bandwidth-bound), so both kinds of work share the CUs instead of
+// running back to back.
+struct MixedParams {
+  PrefillParams pp;
+  DecodeParams dp;
+  int n_prefill;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mixed(MixedParams m) {
+  constexpr int DEC = DecodeLds<2, D, G>::BYTES;
+  constexpr int PRE = PrefillLds<D, G>::BYTES;
+  __shared__ __align__(16) char lds[PRE > 4 * DEC ? PRE : 4 * DEC];
+  if ((int)blockIdx.x < m.n_prefill) {
+    prefill_item<D, G>(m.pp, blockIdx.x, lds);
+  } else {
+    const int wave = threadIdx.x >> 6;
+    const int item = ((int)blockIdx.x - m.n_prefill) * 4 + wave;
+    decode_item<2, D, G>(m.dp, item, lds + wave * DEC);
+  }
+}
+
 template <int D>
 static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
   switch (G) {
@@ -985,9 +1071,7 @@ static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
-  if (a.prefill_tiles == 0) return hipSuccess;
-  if (c.dtype_bytes != 2) return hipErrorInvalidValue;
+static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) {
   PrefillParams p;
   p.kv = c.kv;
   p.block_bytes = c.block_bytes;
@@ -1000,10 +1084,51 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
   p.qsl = a.query_start_loc;
   p.num_seqs = a.num_seqs;
   p.scale_log2 = a.scale * kLog2e;
+  return p;
+}
+
+hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  if (a.prefill_tiles == 0) return hipSuccess;
+  if (c.dtype_bytes != 2) return hipErrorInvalidValue;
+  const PrefillParams p = make_prefill_params(c, a);
   const int G = a.hq / c.hkv;
   const int64_t grid = a.prefill_tiles * c.hkv;
   if (c.head_size == 128) return prefill_g<128>(G, p, grid, stream);
   if (c.head_size == 64) return prefill_g<64>(G, p, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int D, int G>
+static hipError_t mixed_t(const MixedParams& m, int64_t grid, int num_seqs, int hkv,
+                          hipStream_t stream) {
+  hipLaunchKernelGGL((k_mixed<D, G>), dim3((unsigned)grid), dim3(256), 0, stream, m);
+  hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((int64_t)num_seqs * hkv)),
+                     dim3(64 * (G < 4 ? G : 4)), 0, stream, m.dp);
+  return hipGetLastError();
+}
+
+hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  if (c.dtype_bytes != 2) return hipErrorInvalidValue;
+  MixedParams m;
+  m.pp = make_prefill_params(c, a);
+  m.dp = make_decode_params(c, a);
+  m.n_prefill = (int)(a.prefill_tiles * c.hkv);
+  const int64_t decode_wgs = (a.decode_units * c.hkv + 3) / 4;
+  const int64_t grid = m.n_prefill + decode_wgs;
+  const int G = a.hq / c.hkv;
+  if (c.head_size == 128) {
+    switch (G) {
+      case 1: return mixed_t<128, 1>(m, grid, a.num_seqs, c.hkv, stream);
+      case 2: return mixed_t<128, 2>(m, grid, a.num_seqs, c.hkv, stream);
+      case 4: return mixed_t<128, 4>(m, grid, a.num_seqs, c.hkv, stream);
+    }
+  } else if (c.head_size == 64) {
+    switch (G) {
+      case 1: return mixed_t<64, 1>(m, grid, a.num_seqs, c.hkv, stream);
+      case 2: return mixed_t<64, 2>(m, grid, a.num_seqs, c.hkv, stream);
+      case 4: return mixed_t<64, 4>(m, grid, a.num_seqs, c.hkv, stream);
+    }
+  }
   return hipErrorInvalidValue;
 }
 
