@@ -727,20 +727,37 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
 // Prefill rows of a mixed batch (chunked prefill, juhe.plus section 4.2):
 // sequence s has q_len > 1 query rows at positions L - q_len .. L - 1, each
 // seeing keys 0..its position.  Both products are dense here, so they run
-// on MFMA (v_mfma_f32_32x32x16_bf16):
-//   S^T = K Q^T   (32 keys x 32 query rows per tile, k = head dim)
-//   O^T += V^T P^T (32 d x 32 query rows, k = keys)
+// on MFMA:
+//   S^T = K Q^T    v_mfma_f32_32x32x16_bf16 (32 keys x 32 query rows, k = d)
+//   O^T += V^T P^T v_mfma_f32_32x32x16_f16  (32 d x 32 query rows, k = keys)
 // Computing S transposed leaves each lane with one query row, so the
 // softmax row max needs a single exchange between the two 32-lane halves,
 // and the S^T accumulator is already the B operand of the second product.
-// P is split into bf16 hi + lo parts (two MFMAs) so probabilities keep
-// about 16 significant bits; V enters exactly.
+//
+// Precision of P.V: probabilities and V enter the second product as fp16
+// (11 significant bits; bf16's 8 would leave a relative error near 1e-3).
+// bf16 V converts to fp16 exactly while |v| < 2^16 and to +-inf beyond, so
+// a work item whose outputs come out non-finite is run again in a guarded
+// mode: there each key tile's V is scaled by a power of two 2^-k (exact)
+// that brings it below 2^16, the accumulator counts in units of 2^k, and k
+// only grows.  The row sums l are accumulated from the same rounded fp16
+// probabilities that enter the MFMA (v_dot2c_f32_f16), so the normalisation
+// matches the weights used.
+//
 // One workgroup = 4 waves = one kv head x TQ positions; wave w takes query
 // head w % G of the group and positions 32*(w / G) .. +31 of the tile.
-// Keys arrive 64 at a time (4 blocks) through the block table into LDS,
-// K as [key][d] and V as [d][key].
+// Keys arrive 64 at a time (4 blocks) through the block table into LDS:
+// K as [key][d] bf16, V^T as [d][key] fp16 with the keys of each 16-key
+// block stored in the order the MFMA operand wants (0-3, 8-11, 4-7, 12-15),
+// so each operand fragment is one 16-byte LDS read.  Two LDS stages: tile
+// t + 1 is stored while tile t is computed, tile t + 2 is in flight to
+// registers, and the block ids of the tile after that are already loaded,
+// so one workgroup barrier per tile suffices.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 struct PrefillParams {
@@ -766,6 +783,12 @@ struct PrefillShape {
   static constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;             // 32-row d blocks of O^T
   static constexpr int TILE = BS * D * 2;       // bytes of one K or V tile in HBM
+  static constexpr int KGR = 2 * D;             // 16-byte granules of one block's K tile
+  static constexpr int NGK = 4 * KGR / 256;     // K granules per thread per LDS tile
+  static constexpr int KSTEP = 256 / KGR;       // blocks between a thread's K granules
+  static constexpr int NBV = D / 64;            // blocks per thread for V (both granules)
+  static constexpr int STAGE = KT * KROW + D * VROW;  // one K tile + one V^T tile
+  static constexpr int FLAGS = 2 * STAGE;              // 4 maxima + 4 flags (floats)
 };
 
 // Find (sequence, item, items of that sequence) of work item u, where
@@ -799,26 +822,46 @@ __device__ bool find_item(int u, int num_seqs, F count, int& s_out, int& item_ou
   return false;
 }
 
-__device__ __forceinline__ uint32_t pack_hi(float a, float b) {
-  return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
-}
-
 template <int D, int G>
 struct PrefillLds {
-  static constexpr int BYTES = PrefillShape<D, G>::KT * PrefillShape<D, G>::KROW +
-                               D * PrefillShape<D, G>::VROW;
+  static constexpr int BYTES = PrefillShape<D, G>::FLAGS + 32;
 };
 
+// Max of the two 32-lane halves of the wave, in every lane.
+__device__ __forceinline__ float half_swap_max(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float v) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                   false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Two fp32 -> two fp16 (round to nearest even) packed in one dword.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// Two bf16 -> fp16 times `sc` (a power of two) packed in one dword.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float sc) {
+  return pack_f16x2(bf16_lo(w) * sc, bf16_hi(w) * sc);
+}
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(bf16_lo(w), bf16_hi(w));
+}
+__device__ __forceinline__ float bf16x2_absmax(uint32_t w) {
+  return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
+}
+
 // One prefill work item (q tile, kv head) on a whole 4-wave workgroup; `lds`
-// holds the K tile then the V^T tile.
+// holds the K tile, the V^T tile and the per-wave range flags.
 template <int D, int G>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds) {
   using S = PrefillShape<D, G>;
   static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
-  constexpr int KGR = 2 * D;           // 16-byte granules per K (or V) tile of one block
-  constexpr int NG = 4 * KGR / 256;    // granules of K (and of V) per thread per LDS tile
-  char* k_lds = lds;
-  char* v_lds = lds + S::KT * S::KROW;
+  float* flag_lds = reinterpret_cast<float*>(lds + S::FLAGS);  // [0,4): maxima, [4,8): flags
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -835,9 +878,9 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   tile = ntiles - 1 - tile;  // later tiles see more keys: dispatch them first
 
   const int hq = p.hkv * G;
-  const int L = p.seq_lens[s];
-  const int row0 = qsl[s];
-  const int ql = qsl[s + 1] - row0;
+  const int L = uniform(p.seq_lens[s]);
+  const int row0 = uniform(qsl[s]);
+  const int ql = uniform(qsl[s + 1]) - row0;
   const int qfirst = L - ql;                       // position of query row 0
   const int p0 = qfirst + tile * S::TQ;
   const int pend = min(qfirst + ql, p0 + S::TQ);   // positions [p0, pend)
@@ -848,81 +891,173 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   const int r = lane & 31;
   const int my_pos = wp0 + r;
   const bool row_ok = my_pos < pend;
+  const int lim = row_ok ? my_pos : -1;            // last key this row sees
   const int head = kvh * G + g;
+
+  // A negative scale is carried by negating q (exact), so that c > 0 and
+  // the largest raw score is the largest scaled one; a zero scale becomes
+  // the least normal float, so masked scores (-inf) still give exp2 = 0.
+  const bool neg = p.scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
 
   // Q^T operand: lane (h, r) holds q[row r][16 ks + 8 h .. + 8] for every ks.
   bf16x8_t qb[S::KS];
   {
     const size_t tok = (size_t)row0 + (size_t)(row_ok ? my_pos - qfirst : 0);
     const uint4* qrow = reinterpret_cast<const uint4*>(p.q + (tok * hq + head) * D);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-      const uint4 v = row_ok ? qrow[2 * ks + h] : make_uint4(0, 0, 0, 0);
+      uint4 v = row_ok ? qrow[2 * ks + h] : make_uint4(0, 0, 0, 0);
+      v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
       qb[ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
-  f32x16_t o[S::DB];
-#pragma unroll
-  for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
-  float m_run = -1e30f;
-  float l_run = 0.f;
-
   const int kend = pend;                 // keys 0 .. pend - 1 are needed
   const int nkt = (kend + S::KT - 1) / S::KT;
+  const int nblk = (kend + BS - 1) / BS; // blocks of the table in use
   const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
   const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
 
-  // ---- K/V of one 64-key tile: global -> registers (issued a tile ahead),
-  // then registers -> LDS.  Keys at or past L (never written) are zeroed in
-  // V, since 0 * NaN would poison the MFMA sums; K there is masked instead.
-  uint4 kst[NG], vst[NG];
+  // Fixed roles of this thread in every tile load.
+  //   K: granule kw of blocks kb0 + i * KSTEP   (kw = 16 * d-granule + token)
+  //   V: both 8-key granules of d = vd of blocks vb0 .. vb0 + NBV - 1
+  const int kw = tid % S::KGR;
+  const int kb0 = uniform(tid / S::KGR);
+  const int vd = tid % D;
+  const int vb0 = uniform((tid / D) * S::NBV);
+  const uint32_t k_goff = (uint32_t)kw * 16;
+  const uint32_t v_goff = (uint32_t)S::TILE + (uint32_t)vd * 16;
+
+  f32x16_t o[S::DB];
+  float m_run, l_run;
+  int kexp;  // in guarded mode the V^T tiles and o count in units of 2^kexp
+
+  uint4 kst[S::NGK], vst[S::NBV][2];
+  // Lanes 0..3 hold the block ids of the next tile to load.
+  int idv = 0;
+  auto load_ids = [&](int kt) {
+    const int blk = kt * 4 + (lane & 3);
+    idv = blk < nblk ? bt[blk] : 0;
+  };
   auto gload = [&](int kt) {
+    const int32_t id4[4] = {__builtin_amdgcn_readlane(idv, 0), __builtin_amdgcn_readlane(idv, 1),
+                            __builtin_amdgcn_readlane(idv, 2), __builtin_amdgcn_readlane(idv, 3)};
+    auto block_ptr = [&](int bl) { return head_base + (size_t)id4[bl] * p.block_bytes; };
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int gi = tid + 256 * i;
-      const int bl = gi / KGR;
-      const int blk = kt * 4 + bl;
-      const int within = gi % KGR;
-      kst[i] = make_uint4(0, 0, 0, 0);
-      vst[i] = make_uint4(0, 0, 0, 0);
-      if (blk * BS < kend) {
-        const char* base = head_base + (size_t)bt[blk] * p.block_bytes;
-        const int c = within / BS, t = within % BS;
-        kst[i] = *reinterpret_cast<const uint4*>(base + (c * BS + t) * 16);
-        const int kg = within / D, d = within % D;
-        uint4 v = *reinterpret_cast<const uint4*>(base + S::TILE + (kg * D + d) * 16);
-        const int key0 = blk * BS + kg * 8;
-        if (key0 + 8 > L) {
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int i = 0; i < S::NGK; ++i) {
+      const int bl = kb0 + i * S::KSTEP;
+      kst[i] = kt * 4 + bl < nblk ? *reinterpret_cast<const uint4*>(block_ptr(bl) + k_goff)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int b = 0; b < S::NBV; ++b) {
+      const int bl = vb0 + b;
+      if (kt * 4 + bl < nblk) {
+        const char* base = block_ptr(bl) + v_goff;
+        vst[b][0] = *reinterpret_cast<const uint4*>(base);
+        vst[b][1] = *reinterpret_cast<const uint4*>(base + D * 16);
+      } else {
+        vst[b][0] = make_uint4(0, 0, 0, 0);
+        vst[b][1] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    load_ids(kt + 1);
+  };
+  // Keys at or past L (never written, possibly NaN) are zeroed in V, since
+  // 0 * NaN would poison the MFMA sums; K there is masked instead.
+  auto mask_tail = [&](int kt) {
+#pragma unroll
+    for (int b = 0; b < S::NBV; ++b) {
+      const int blk = kt * 4 + vb0 + b;
+      if (blk * BS + BS > L) {
+#pragma unroll
+        for (int kg = 0; kg < 2; ++kg) {
+          uint32_t w[4] = {vst[b][kg].x, vst[b][kg].y, vst[b][kg].z, vst[b][kg].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+            if (blk * BS + kg * 8 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+          vst[b][kg] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        vst[i] = v;
       }
     }
   };
-  auto lstore = [&]() {
+  // Largest |v| among this thread's V values of the loaded tile.
+  auto v_absmax = [&]() {
+    float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int gi = tid + 256 * i;
-      const int bl = gi / KGR;
-      const int within = gi % KGR;
-      const int c = within / BS, t = within % BS;
-      *reinterpret_cast<uint4*>(k_lds + (bl * BS + t) * S::KROW + c * 16) = kst[i];
-      const int kg = within / D, d = within % D;
-      *reinterpret_cast<uint4*>(v_lds + d * S::VROW + (bl * BS + kg * 8) * 2) = vst[i];
+    for (int b = 0; b < S::NBV; ++b)
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+        m = fmaxf(m, fmaxf(fmaxf(bf16x2_absmax(vst[b][kg].x), bf16x2_absmax(vst[b][kg].y)),
+                           fmaxf(bf16x2_absmax(vst[b][kg].z), bf16x2_absmax(vst[b][kg].w))));
+    return m;
+  };
+  // Registers -> LDS; V converted to fp16 (times 2^-kexp when scaled) and
+  // reordered within each block.
+  auto lstore = [&](char* k_lds, bool scaled, float sc) {
+    char* v_lds = k_lds + S::KT * S::KROW;
+#pragma unroll
+    for (int i = 0; i < S::NGK; ++i) {
+      const int bl = kb0 + i * S::KSTEP;
+      *reinterpret_cast<uint4*>(k_lds + (bl * BS + kw % BS) * S::KROW + (kw / BS) * 16) = kst[i];
+    }
+#pragma unroll
+    for (int b = 0; b < S::NBV; ++b) {
+      uint32_t f[2][4];
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+        const uint32_t w[4] = {vst[b][kg].x, vst[b][kg].y, vst[b][kg].z, vst[b][kg].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[kg][e] = scaled ? bf16x2_to_f16x2(w[e], sc) : bf16x2_to_f16x2(w[e]);
+      }
+      char* row = v_lds + vd * S::VROW + (vb0 + b) * 32;
+      *reinterpret_cast<uint4*>(row) = make_uint4(f[0][0], f[0][1], f[1][0], f[1][1]);
+      *reinterpret_cast<uint4*>(row + 16) = make_uint4(f[0][2], f[0][3], f[1][2], f[1][3]);
+    }
+  };
+  // The loaded tile goes to LDS stage `st`.  Call with every wave past its
+  // last read of that stage; a barrier follows before anyone reads it.  In
+  // guarded mode the tile's largest |v| is found workgroup-wide (every wave
+  // takes the same decisions) and the tile gets the smallest scale exponent,
+  // not below the previous tile's, that brings it under 2^16.
+  int kst_exp[2] = {0, 0};  // scale exponent of the tile in each stage
+  int kpub = 0;             // exponent of the last tile published
+  auto publish = [&](int kt, int st, bool guarded) {
+    if (kt * S::KT + S::KT > L) mask_tail(kt);
+    char* stage = lds + st * S::STAGE;
+    if (!guarded) {
+      lstore(stage, false, 1.f);
+      return;
+    }
+    const float wm = wave_max(v_absmax());
+    if (lane == 0) flag_lds[wave] = wm;
+    __syncthreads();
+    const float4 mm = *reinterpret_cast<const float4*>(flag_lds);
+    const float tmax = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
+    // smallest k with tmax * 2^-k < 2^16, bounded for non-finite maxima
+    // (whose results are then non-finite as in exact arithmetic)
+    const int e = (int)((__float_as_uint(tmax) >> 23) & 0xff) - 127;
+    kpub = max(kpub, min(max(e - 15, 0), 100));
+    kst_exp[st] = kpub;
+    lstore(stage, true, __builtin_ldexpf(1.f, -kpub));
+  };
+  // Brings the accumulator to the scale of the tile about to be used.
+  auto align_scale = [&](int st) {
+    if (kst_exp[st] > kexp) {
+      const float corr = __builtin_ldexpf(1.f, kexp - kst_exp[st]);
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
+      kexp = kst_exp[st];
     }
   };
 
-  // ---- one 32-key chunk: scores S^T (MFMA), online softmax, P split into
-  // bf16 hi + lo, O^T += V^T P^T (MFMA).
-  auto scores = [&](int j, f32x16_t& sacc) {
+  // ---- one 32-key chunk: scores S^T (MFMA), online softmax, P in fp16,
+  // O^T += V^T P^T (MFMA).
+  auto scores = [&](const char* k_lds, int j, f32x16_t& sacc) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
     const char* krow = k_lds + (32 * j + r) * S::KROW + h * 16;
@@ -933,89 +1068,113 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
                                                      0, 0, 0);
     }
   };
-  auto softmax_pv = [&](int k0, int j, const f32x16_t& sacc) {
+  // Lane (h, r) holds S^T[key kj + 8 (i / 4) + 4 h + i % 4][row r], i < 16.
+  auto softmax_pv = [&](const char* k_lds, int k0, int j, f32x16_t& sacc) {
+    const char* v_lds = k_lds + S::KT * S::KROW;
     const int kj = k0 + 32 * j;
-    float x[16];
-    float mt = -INFINITY;
+    if (__builtin_expect(kj + 31 > wp0, 0)) {  // wave-uniform: the chunk reaches the diagonal
+      const int kl = lim - (kj + 4 * h);  // key offsets in the chunk up to kl are visible
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kj + 8 * (i >> 2) + 4 * h + (i & 3);
-      x[i] = (row_ok && key <= my_pos) ? sacc[i] * p.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, x[i]);
+      for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) <= kl) ? sacc[i] : -INFINITY;
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    float mt = fmaxf(fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])),
+                     fmaxf(fmaxf(sacc[4], sacc[5]), fmaxf(sacc[6], sacc[7])));
+    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sacc[8], sacc[9]), fmaxf(sacc[10], sacc[11])),
+                         fmaxf(fmaxf(sacc[12], sacc[13]), fmaxf(sacc[14], sacc[15]))));
+    mt = half_swap_max(mt) * c;
     const bool need = mt > m_run + kRescaleSlack;
     if (__ballot(need)) {
-      const float corr = need ? __builtin_amdgcn_exp2f(m_run - mt) : 1.f;
-      m_run = need ? mt : m_run;
+      const float mnew = need ? mt : m_run;
+      const float corr = __builtin_amdgcn_exp2f(m_run - mnew);
+      m_run = mnew;
       l_run *= corr;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= corr;
     }
-    uint32_t phi[2][4], plo[2][4];
+    const float nm = -m_run;
+    const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
+    uint32_t pk[8];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float a = __builtin_amdgcn_exp2f(x[8 * kk + 2 * m] - m_run);
-        const float b = __builtin_amdgcn_exp2f(x[8 * kk + 2 * m + 1] - m_run);
-        l_run += a + b;
-        const float ah = __uint_as_float(__float_as_uint(a) & 0xffff0000u);
-        const float bh = __uint_as_float(__float_as_uint(b) & 0xffff0000u);
-        phi[kk][m] = pack_hi(ah, bh);
-        plo[kk][m] = pack_hi(a - ah, b - bh);
-      }
+    for (int w = 0; w < 8; ++w) {
+      pk[w] = pack_f16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w], c, nm)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w + 1], c, nm)));
+      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[w]), one, l_run, false);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t bh = __builtin_bit_cast(bf16x8_t, make_uint4(phi[kk][0], phi[kk][1], phi[kk][2], phi[kk][3]));
-      const bf16x8_t bl = __builtin_bit_cast(bf16x8_t, make_uint4(plo[kk][0], plo[kk][1], plo[kk][2], plo[kk][3]));
-      bf16x8_t a[S::DB];
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db) {
-        const char* vrow = v_lds + (32 * db + r) * S::VROW + (32 * j + 16 * kk + 4 * h) * 2;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(vrow + 16);
-        a[db] = __builtin_bit_cast(bf16x8_t, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-      }
+      const f16x8_t bop = __builtin_bit_cast(
+          f16x8_t, make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
+      f16x8_t a[S::DB];
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], bh, o[db], 0, 0, 0);
+        a[db] = __builtin_bit_cast(
+            f16x8_t, *reinterpret_cast<const uint4*>(v_lds + (32 * db + r) * S::VROW +
+                                                      (2 * j + kk) * 32 + h * 16));
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db], bl, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], bop, o[db], 0, 0, 0);
     }
   };
 
-  gload(0);
-  lstore();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int k0 = kt * S::KT;
-    if (kt + 1 < nkt) gload(kt + 1);  // in flight while this tile is computed
-    if (k0 <= wlast) {
-      // both chunks' scores first, so the softmax of chunk 0 overlaps the
-      // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
-      const bool two = k0 + 32 <= wlast;
-      f32x16_t s0, s1;
-      scores(0, s0);
-      if (two) scores(1, s1);
-      softmax_pv(k0, 0, s0);
-      if (two) softmax_pv(k0, 1, s1);
+  // Pass 0 runs unguarded; pass 1 (guarded) only if some output of pass 0
+  // came out non-finite, which a V value of magnitude >= 2^16 causes.
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool guarded = pass == 1;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
+    m_run = -1e30f;
+    l_run = 0.f;
+    kexp = 0;
+    kpub = 0;
+    kst_exp[0] = kst_exp[1] = 0;
+
+    load_ids(0);
+    gload(0);
+    publish(0, 0, guarded);
+    if (nkt > 1) gload(1);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int st = kt & 1;
+      if (kt + 1 < nkt) publish(kt + 1, st ^ 1, guarded);  // its stage was freed last barrier
+      if (kt + 2 < nkt) gload(kt + 2);                     // in flight while this tile is computed
+      const int k0 = kt * S::KT;
+      if (k0 <= wlast) {
+        const char* stage = lds + st * S::STAGE;
+        if (guarded) align_scale(st);
+        // both chunks' scores first, so the softmax of chunk 0 overlaps the
+        // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
+        const bool two = k0 + 32 <= wlast;
+        f32x16_t s0, s1;
+        scores(stage, 0, s0);
+        if (two) scores(stage, 1, s1);
+        softmax_pv(stage, k0, 0, s0);
+        if (two) softmax_pv(stage, k0, 1, s1);
+      }
+      __syncthreads();  // tile kt + 1 is stored; every wave is done with tile kt
     }
-    __syncthreads();  // every wave is done with this tile
-    if (kt + 1 < nkt) {
-      lstore();
-      __syncthreads();
-    }
+    if (guarded) break;
+    float sum = 0.f;
+#pragma unroll
+    for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += o[db][i];
+    const bool bad = __ballot(row_ok && !__builtin_isfinite(sum)) != 0;
+    if (lane == 0) flag_lds[4 + wave] = bad ? 1.f : 0.f;
+    __syncthreads();
+    const float4 fl = *reinterpret_cast<const float4*>(flag_lds + 4);
+    if (fl.x + fl.y + fl.z + fl.w == 0.f) break;
+    __syncthreads();  // every wave has read the flags and left the last tile
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = half_swap_sum(l_run);
   if (row_ok) {
     float* orow = p.out + (((size_t)row0 + (my_pos - qfirst)) * hq + head) * D;
-    const float inv = 1.f / l_tot;
+    const float inv = __builtin_ldexpf(1.f / l_tot, kexp);
 #pragma unroll
     for (int db = 0; db < S::DB; ++db) {
 #pragma unroll
