@@ -123,9 +123,14 @@ int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, 
 
 /* ------------------------------------------------------------ attention */
 /* Workspace bytes paged_attention_decode / paged_attention_mixed need for
- * these host lengths (split-K partials).  h_query_start_loc may be NULL for
- * a pure decode batch (one query row per sequence); cache->kv may be NULL.
- * 0 on invalid input, and also when no workspace is needed. */
+ * these host lengths: the split-K partials of decode rows (per split row:
+ * (head_size + 2) floats per query head and 256-token partition) and, for
+ * every sequence with q_len > 1, an fp16 copy of the V tiles of its blocks
+ * (rounded up to whole 64-token tiles) with one int32 scale exponent per
+ * (block, kv head).  h_query_start_loc may be NULL for a pure decode batch
+ * (one query row per sequence); cache->kv may be NULL.  0 on invalid input,
+ * and also when no workspace is needed.  A call overwrites the workspace;
+ * calls that may overlap need separate workspaces. */
 size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads,
                                      const int32_t* h_query_start_loc,
                                      const int32_t* h_seq_lens, int32_t num_seqs);

@@ -72,6 +72,7 @@ struct Plan {
   int64_t class_count[pkv::kPartClasses] = {0};
   int64_t prefill_tiles = 0;
   int prefill_seqs = 0;
+  int64_t prefill_vblocks = 0;
   int64_t num_tokens = 0;
 };
 
@@ -104,15 +105,28 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
       const int tq = pkv::prefill_tile_q(group);
       plan->prefill_tiles += (ql + tq - 1) / tq;
       plan->prefill_seqs += 1;
+      plan->prefill_vblocks += pkv::prefill_vblocks(L);
     }
     plan->num_tokens += ql;
   }
   return PKV_OK;
 }
 
-size_t workspace_for(const Plan& p, int hq, int D) {
-  if (p.decode_units == 0) return 0;
-  return pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+// Workspace layout: header | decode partials acc [units][hq][D], (m, l)
+// [units][hq][2] | (256-aligned) fp16 V tiles [vblocks][hkv][16 D] | their
+// exponents [hkv][vblocks].
+struct WsLayout {
+  size_t v_off, exp_off, total;
+};
+WsLayout ws_layout(const Plan& p, int hq, int hkv, int D) {
+  WsLayout w{0, 0, 0};
+  if (p.decode_units == 0 && p.prefill_vblocks == 0) return w;
+  const size_t dec = (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+  w.v_off = (pkv::kWorkspaceHeader + dec + 255) / 256 * 256;
+  w.exp_off = w.v_off + (size_t)p.prefill_vblocks * hkv * pkv::kBlockSize * D * 2;
+  w.total = p.prefill_vblocks ? w.exp_off + (size_t)p.prefill_vblocks * hkv * sizeof(int32_t)
+                              : pkv::kWorkspaceHeader + dec;
+  return w;
 }
 
 
@@ -144,7 +158,8 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   if (!out || !q || !seq_lens || !block_tables || (mixed && !qsl))
     return fail(PKV_ERR_NULL, "a device pointer (out, q, seq_lens, block_tables%s) is NULL",
                 mixed ? ", query_start_loc" : "");
-  const size_t need = workspace_for(plan, num_q_heads, c.head_size);
+  const WsLayout wl = ws_layout(plan, num_q_heads, c.hkv, c.head_size);
+  const size_t need = wl.total;
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
   pkv::AttnDesc a;
@@ -166,6 +181,9 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   for (int k = 0; k < pkv::kPartClasses; ++k) a.class_start[k + 1] = a.class_start[k] + plan.class_count[k];
   a.prefill_tiles = plan.prefill_tiles;
   a.prefill_seqs = plan.prefill_seqs;
+  a.prefill_vblocks = plan.prefill_vblocks;
+  a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;
+  a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.prefill_tiles > 0 && plan.decode_units > 0)
     return hip_status(pkv::launch_mixed_rows(c, a, st), "mixed rows");
@@ -264,7 +282,7 @@ size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads
   if (plan_attention(h_qsl, h_seq_lens, num_seqs, INT32_MAX / pkv::kBlockSize,
                      num_q_heads / c.hkv, &plan))
     return 0;
-  return workspace_for(plan, num_q_heads, c.head_size);
+  return ws_layout(plan, num_q_heads, c.hkv, c.head_size).total;
 }
 
 int paged_attention_decode(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,

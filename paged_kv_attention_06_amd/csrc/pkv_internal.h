@@ -18,6 +18,9 @@ constexpr int prefill_tile_q(int g) { return 128 / g; }
 constexpr int kPartClasses = kPartTokens / 32;
 // Bytes at the start of the attention workspace before the partials.
 constexpr size_t kWorkspaceHeader = 256;
+// Blocks of a prefill sequence of length L whose V the prefill path converts
+// to fp16 (whole 64-key tiles).
+inline int64_t prefill_vblocks(int64_t L) { return 4 * ((L + 4 * kBlockSize - 1) / (4 * kBlockSize)); }
 
 struct CacheDesc {
   char* kv;
@@ -45,6 +48,9 @@ struct AttnDesc {
   int64_t class_start[kPartClasses + 1];  // partial units before size class k
   int64_t prefill_tiles;           // prefill q-tiles over all prefill rows
   int prefill_seqs;                // sequences with more than one query row
+  int64_t prefill_vblocks;         // blocks of the prefill sequences, each rounded up to 4
+  char* ws_v;                      // fp16 V tiles of those blocks [vblock][hkv][16 * D]
+  int32_t* ws_vexp;                // their power-of-two scale exponents [hkv][vblock]
 };
 
 hipError_t launch_kv_write(const CacheDesc& c, const void* k_new, const void* v_new,

@@ -736,29 +736,37 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
 //
 // Precision of P.V: probabilities and V enter the second product as fp16
 // (11 significant bits; bf16's 8 would leave a relative error near 1e-3).
-// bf16 V converts to fp16 exactly while |v| < 2^16 and to +-inf beyond, so
-// a work item whose outputs come out non-finite is run again in a guarded
-// mode: there each key tile's V is scaled by a power of two 2^-k (exact)
-// that brings it below 2^16, the accumulator counts in units of 2^k, and k
-// only grows.  The row sums l are accumulated from the same rounded fp16
-// probabilities that enter the MFMA (v_dot2c_f32_f16), so the normalisation
-// matches the weights used.
+// A first pass (k_v_fp16) converts the V tiles of every prefill sequence's
+// blocks once, through the block table, into the workspace: each block
+// tile is scaled by the power of two 2^-e (exact) that keeps it below 2^16,
+// e is recorded per (kv head, block), and keys past the sequence length are
+// zeroed.  The tile kernel keeps its accumulator in units of 2^kexp and
+// adjusts P or the accumulator by exact powers of two when a block's e
+// differs (all e are 0 unless some |v| >= 2^16).  The row sums l come from
+// the same rounded fp16 probabilities that enter the MFMA (v_dot2c_f32_f16,
+// before any such adjustment), so the normalisation matches the weights.
 //
 // One workgroup = 4 waves = one kv head x TQ positions; wave w takes query
 // head w % G of the group and positions 32*(w / G) .. +31 of the tile.
-// Keys arrive 64 at a time (4 blocks) through the block table into LDS:
-// K as [key][d] bf16, V^T as [d][key] fp16 with the keys of each 16-key
-// block stored in the order the MFMA operand wants (0-3, 8-11, 4-7, 12-15),
-// so each operand fragment is one 16-byte LDS read.  Two LDS stages: tile
-// t + 1 is stored while tile t is computed, tile t + 2 is in flight to
-// registers, and the block ids of the tile after that are already loaded,
-// so one workgroup barrier per tile suffices.
+// Keys arrive 64 at a time (4 blocks): wave w copies block w's K tile
+// (from the pool, through the block table) and fp16 V tile (from the
+// workspace) straight into LDS with global_load_lds_dwordx4, in their HBM
+// layouts, two stages deep, so one barrier per tile suffices and no
+// registers stage the data.  The K operand's lane r reads key pi(r), where
+// pi swaps bits 2 and 3 of r: the S^T rows a lane then holds are the 8
+// consecutive keys of one V granule, which is the k order of the second
+// product's operands, so both operand fragments are single 16-byte reads.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+// Scalar-cache view of read-only device arrays whose index is wave-uniform.
+typedef const __attribute__((address_space(4))) int32_t sint32_t;
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(4))) i32x4_t sint4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct PrefillParams {
   const char* kv;
@@ -772,23 +780,25 @@ struct PrefillParams {
   const int32_t* qsl;
   int num_seqs;
   float scale_log2;
+  char* vh;          // fp16 V tiles [vblock][hkv][16 * D], vblock = sequence-major
+  int32_t* vexp;     // scale exponents [hkv][vblocks]
+  int64_t vblocks;   // blocks of all prefill sequences, each rounded up to 4
 };
 
 template <int D, int G>
 struct PrefillShape {
   static constexpr int TQ = prefill_tile_q(G);  // query positions per workgroup
-  static constexpr int KT = 64;                 // keys per LDS tile (4 blocks)
-  static constexpr int KROW = D * 2 + 16;       // LDS bytes per key row of K (padded)
-  static constexpr int VROW = KT * 2 + 16;      // LDS bytes per d row of V^T (padded)
+  static constexpr int KT = 64;                 // keys per tile (4 blocks)
   static constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;             // 32-row d blocks of O^T
-  static constexpr int TILE = BS * D * 2;       // bytes of one K or V tile in HBM
-  static constexpr int KGR = 2 * D;             // 16-byte granules of one block's K tile
-  static constexpr int NGK = 4 * KGR / 256;     // K granules per thread per LDS tile
-  static constexpr int KSTEP = 256 / KGR;       // blocks between a thread's K granules
-  static constexpr int NBV = D / 64;            // blocks per thread for V (both granules)
-  static constexpr int STAGE = KT * KROW + D * VROW;  // one K tile + one V^T tile
-  static constexpr int FLAGS = 2 * STAGE;              // 4 maxima + 4 flags (floats)
+  static constexpr int TILE = BS * D * 2;       // bytes of one block's K (or fp16 V) tile
+  static constexpr int STAGE = 8 * TILE;        // 4 K tiles then 4 V tiles
+  static constexpr int CP = TILE / 1024;        // 1 KiB copies per tile and wave
+};
+
+template <int D, int G>
+struct PrefillLds {
+  static constexpr int STAGE = PrefillShape<D, G>::STAGE;  // bytes of each of the two stages
 };
 
 // Find (sequence, item, items of that sequence) of work item u, where
@@ -822,10 +832,25 @@ __device__ bool find_item(int u, int num_seqs, F count, int& s_out, int& item_ou
   return false;
 }
 
-template <int D, int G>
-struct PrefillLds {
-  static constexpr int BYTES = PrefillShape<D, G>::FLAGS + 32;
-};
+// Sum of count(q) over sequences q < s (wave-level; every lane gets it).
+template <typename F>
+__device__ int count_before(int s, F count) {
+  const int lane = threadIdx.x & 63;
+  int sum = 0;
+  for (int s0 = 0; s0 < s; s0 += 64) {
+    int v = (s0 + lane < s) ? count(s0 + lane) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    sum += v;
+  }
+  return uniform(sum);
+}
+
+// Blocks of prefill sequence q converted by k_v_fp16 (0 for decode rows).
+__device__ __forceinline__ int prefill_vblocks_of(const PrefillParams& p, int q) {
+  const int ql = p.qsl[q + 1] - p.qsl[q];
+  return ql > 1 ? 4 * ((p.seq_lens[q] + 4 * BS - 1) / (4 * BS)) : 0;
+}
 
 // Max of the two 32-lane halves of the wave, in every lane.
 __device__ __forceinline__ float half_swap_max(float v) {
@@ -844,28 +869,82 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const f32x2_t v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
-// Two bf16 -> fp16 times `sc` (a power of two) packed in one dword.
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float sc) {
-  return pack_f16x2(bf16_lo(w) * sc, bf16_hi(w) * sc);
-}
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  return pack_f16x2(bf16_lo(w), bf16_hi(w));
-}
 __device__ __forceinline__ float bf16x2_absmax(uint32_t w) {
   return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
 }
 
-// One prefill work item (q tile, kv head) on a whole 4-wave workgroup; `lds`
-// holds the K tile, the V^T tile and the per-wave range flags.
+// ---- V tiles of the prefill sequences -> fp16 in the workspace.  One wave
+// per (vblock, kv head): the tile's 16 * D values, keys >= L zeroed, scaled
+// by 2^-e with e the smallest exponent that brings every |v| below 2^16.
+template <int D>
+__global__ __launch_bounds__(256) void k_v_fp16(PrefillParams p) {
+  constexpr int TILE = BS * D * 2;
+  constexpr int NG = TILE / 16 / 64;  // granules per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= p.vblocks * p.hkv) return;
+  const int kvh = (int)(item % p.hkv);
+  const int vb = (int)(item / p.hkv);
+  int s, j, n;
+  if (!find_item(vb, p.num_seqs, [&p](int q) { return prefill_vblocks_of(p, q); }, s, j, n)) return;
+  const int L = uniform(p.seq_lens[s]);
+  uint4 g[NG];
+  if (j * BS < L) {
+    const int id = uniform(p.block_tables[(size_t)s * p.max_blocks + j]);
+    const char* src = p.kv + (size_t)id * p.block_bytes + (size_t)(2 * kvh + 1) * TILE;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) g[i] = *reinterpret_cast<const uint4*>(src + (lane + 64 * i) * 16);
+    if (j * BS + BS > L) {
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        const int key0 = j * BS + ((lane + 64 * i) / D) * 8;  // granule = 8 keys of one d
+        uint32_t w[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        g[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NG; ++i) g[i] = make_uint4(0, 0, 0, 0);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < NG; ++i)
+    m = fmaxf(m, fmaxf(fmaxf(bf16x2_absmax(g[i].x), bf16x2_absmax(g[i].y)),
+                       fmaxf(bf16x2_absmax(g[i].z), bf16x2_absmax(g[i].w))));
+  m = wave_max(m);
+  // smallest e >= 0 with m * 2^-e < 2^16; non-finite maxima get a bounded e
+  // (their results are then non-finite as in exact arithmetic)
+  const int ex = (int)((__float_as_uint(m) >> 23) & 0xff) - 127;
+  const int e = min(max(ex - 15, 0), 100);
+  const float sc = __builtin_ldexpf(1.f, -e);
+  char* dst = p.vh + ((size_t)vb * p.hkv + kvh) * TILE;
+#pragma unroll
+  for (int i = 0; i < NG; ++i) {
+    const uint4 v = g[i];
+    *reinterpret_cast<uint4*>(dst + (lane + 64 * i) * 16) = make_uint4(
+        pack_f16x2(bf16_lo(v.x) * sc, bf16_hi(v.x) * sc), pack_f16x2(bf16_lo(v.y) * sc, bf16_hi(v.y) * sc),
+        pack_f16x2(bf16_lo(v.z) * sc, bf16_hi(v.z) * sc), pack_f16x2(bf16_lo(v.w) * sc, bf16_hi(v.w) * sc));
+  }
+  if (lane == 0) p.vexp[(size_t)kvh * p.vblocks + vb] = e;
+}
+
+// One prefill work item (q tile, kv head) on a whole 4-wave workgroup;
+// `lds0` and `lds1` are the two stages (4 K tiles + 4 fp16 V tiles each).
+// They must be distinct __shared__ arrays: the compiler then sees that the
+// copies into one stage cannot alias the reads of the other and does not
+// make the reads wait for those copies.
 template <int D, int G>
-__device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds) {
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds0,
+                                             char* lds1) {
   using S = PrefillShape<D, G>;
   static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
-  float* flag_lds = reinterpret_cast<float*>(lds + S::FLAGS);  // [0,4): maxima, [4,8): flags
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int kvh = work % p.hkv;
   const int item = work / p.hkv;
   int s, tile, ntiles;
@@ -876,6 +955,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   };
   if (!find_item(item, p.num_seqs, tiles_of, s, tile, ntiles)) return;
   tile = ntiles - 1 - tile;  // later tiles see more keys: dispatch them first
+  const int vbase = count_before(s, [&p](int q) { return prefill_vblocks_of(p, q); });
 
   const int hq = p.hkv * G;
   const int L = uniform(p.seq_lens[s]);
@@ -914,173 +994,94 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
     }
   }
 
-  const int kend = pend;                 // keys 0 .. pend - 1 are needed
-  const int nkt = (kend + S::KT - 1) / S::KT;
-  const int nblk = (kend + BS - 1) / BS; // blocks of the table in use
-  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
-  const char* head_base = p.kv + (size_t)kvh * 2 * S::TILE;
+  const int nkt = (pend + S::KT - 1) / S::KT;      // key tiles needed (keys < pend)
+  const int nbl = (L + BS - 1) / BS;               // valid block-table entries
+  sint32_t* bt = (sint32_t*)(p.block_tables + (size_t)s * p.max_blocks);
+  const char* k_src = p.kv + (size_t)kvh * 2 * S::TILE + lane * 16;
+  const char* v_src = p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
+  sint4_t* vexp4 = (sint4_t*)(p.vexp + (size_t)kvh * p.vblocks + vbase);
 
-  // Fixed roles of this thread in every tile load.
-  //   K: granule kw of blocks kb0 + i * KSTEP   (kw = 16 * d-granule + token)
-  //   V: both 8-key granules of d = vd of blocks vb0 .. vb0 + NBV - 1
-  const int kw = tid % S::KGR;
-  const int kb0 = uniform(tid / S::KGR);
-  const int vd = tid % D;
-  const int vb0 = uniform((tid / D) * S::NBV);
-  const uint32_t k_goff = (uint32_t)kw * 16;
-  const uint32_t v_goff = (uint32_t)S::TILE + (uint32_t)vd * 16;
+  // ---- wave w copies block w of a tile: its K tile from the pool (blocks
+  // past the table are left stale: their keys are masked) and its fp16 V
+  // tile from the workspace (zero there past L).
+  int id_next = wave < nbl ? bt[wave] : 0;  // block id for the next copy
+  auto issue = [&](int kt, char* stage) {
+    char* kd = stage + wave * S::TILE;
+    char* vd = kd + 4 * S::TILE;
+    const int blk = kt * 4 + wave;
+    if (blk < nbl) {
+      const char* ks = k_src + (size_t)id_next * p.block_bytes;
+#pragma unroll
+      for (int i = 0; i < S::CP; ++i)
+        __builtin_amdgcn_global_load_lds(ks + i * 1024, (lds_void_t*)(kd + i * 1024), 16, 0, 0);
+    }
+    const char* vs = v_src + (size_t)blk * p.hkv * S::TILE;
+#pragma unroll
+    for (int i = 0; i < S::CP; ++i)
+      __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
+    id_next = blk + 4 < nbl ? bt[blk + 4] : 0;
+  };
 
   f32x16_t o[S::DB];
-  float m_run, l_run;
-  int kexp;  // in guarded mode the V^T tiles and o count in units of 2^kexp
-
-  uint4 kst[S::NGK], vst[S::NBV][2];
-  // Lanes 0..3 hold the block ids of the next tile to load.
-  int idv = 0;
-  auto load_ids = [&](int kt) {
-    const int blk = kt * 4 + (lane & 3);
-    idv = blk < nblk ? bt[blk] : 0;
-  };
-  auto gload = [&](int kt) {
-    const int32_t id4[4] = {__builtin_amdgcn_readlane(idv, 0), __builtin_amdgcn_readlane(idv, 1),
-                            __builtin_amdgcn_readlane(idv, 2), __builtin_amdgcn_readlane(idv, 3)};
-    auto block_ptr = [&](int bl) { return head_base + (size_t)id4[bl] * p.block_bytes; };
 #pragma unroll
-    for (int i = 0; i < S::NGK; ++i) {
-      const int bl = kb0 + i * S::KSTEP;
-      kst[i] = kt * 4 + bl < nblk ? *reinterpret_cast<const uint4*>(block_ptr(bl) + k_goff)
-                                  : make_uint4(0, 0, 0, 0);
-    }
+  for (int db = 0; db < S::DB; ++db)
 #pragma unroll
-    for (int b = 0; b < S::NBV; ++b) {
-      const int bl = vb0 + b;
-      if (kt * 4 + bl < nblk) {
-        const char* base = block_ptr(bl) + v_goff;
-        vst[b][0] = *reinterpret_cast<const uint4*>(base);
-        vst[b][1] = *reinterpret_cast<const uint4*>(base + D * 16);
-      } else {
-        vst[b][0] = make_uint4(0, 0, 0, 0);
-        vst[b][1] = make_uint4(0, 0, 0, 0);
-      }
-    }
-    load_ids(kt + 1);
-  };
-  // Keys at or past L (never written, possibly NaN) are zeroed in V, since
-  // 0 * NaN would poison the MFMA sums; K there is masked instead.
-  auto mask_tail = [&](int kt) {
-#pragma unroll
-    for (int b = 0; b < S::NBV; ++b) {
-      const int blk = kt * 4 + vb0 + b;
-      if (blk * BS + BS > L) {
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg) {
-          uint32_t w[4] = {vst[b][kg].x, vst[b][kg].y, vst[b][kg].z, vst[b][kg].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (blk * BS + kg * 8 + e >= L) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          vst[b][kg] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-      }
-    }
-  };
-  // Largest |v| among this thread's V values of the loaded tile.
-  auto v_absmax = [&]() {
-    float m = 0.f;
-#pragma unroll
-    for (int b = 0; b < S::NBV; ++b)
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
-        m = fmaxf(m, fmaxf(fmaxf(bf16x2_absmax(vst[b][kg].x), bf16x2_absmax(vst[b][kg].y)),
-                           fmaxf(bf16x2_absmax(vst[b][kg].z), bf16x2_absmax(vst[b][kg].w))));
-    return m;
-  };
-  // Registers -> LDS; V converted to fp16 (times 2^-kexp when scaled) and
-  // reordered within each block.
-  auto lstore = [&](char* k_lds, bool scaled, float sc) {
-    char* v_lds = k_lds + S::KT * S::KROW;
-#pragma unroll
-    for (int i = 0; i < S::NGK; ++i) {
-      const int bl = kb0 + i * S::KSTEP;
-      *reinterpret_cast<uint4*>(k_lds + (bl * BS + kw % BS) * S::KROW + (kw / BS) * 16) = kst[i];
-    }
-#pragma unroll
-    for (int b = 0; b < S::NBV; ++b) {
-      uint32_t f[2][4];
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-        const uint32_t w[4] = {vst[b][kg].x, vst[b][kg].y, vst[b][kg].z, vst[b][kg].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[kg][e] = scaled ? bf16x2_to_f16x2(w[e], sc) : bf16x2_to_f16x2(w[e]);
-      }
-      char* row = v_lds + vd * S::VROW + (vb0 + b) * 32;
-      *reinterpret_cast<uint4*>(row) = make_uint4(f[0][0], f[0][1], f[1][0], f[1][1]);
-      *reinterpret_cast<uint4*>(row + 16) = make_uint4(f[0][2], f[0][3], f[1][2], f[1][3]);
-    }
-  };
-  // The loaded tile goes to LDS stage `st`.  Call with every wave past its
-  // last read of that stage; a barrier follows before anyone reads it.  In
-  // guarded mode the tile's largest |v| is found workgroup-wide (every wave
-  // takes the same decisions) and the tile gets the smallest scale exponent,
-  // not below the previous tile's, that brings it under 2^16.
-  int kst_exp[2] = {0, 0};  // scale exponent of the tile in each stage
-  int kpub = 0;             // exponent of the last tile published
-  auto publish = [&](int kt, int st, bool guarded) {
-    if (kt * S::KT + S::KT > L) mask_tail(kt);
-    char* stage = lds + st * S::STAGE;
-    if (!guarded) {
-      lstore(stage, false, 1.f);
-      return;
-    }
-    const float wm = wave_max(v_absmax());
-    if (lane == 0) flag_lds[wave] = wm;
-    __syncthreads();
-    const float4 mm = *reinterpret_cast<const float4*>(flag_lds);
-    const float tmax = fmaxf(fmaxf(mm.x, mm.y), fmaxf(mm.z, mm.w));
-    // smallest k with tmax * 2^-k < 2^16, bounded for non-finite maxima
-    // (whose results are then non-finite as in exact arithmetic)
-    const int e = (int)((__float_as_uint(tmax) >> 23) & 0xff) - 127;
-    kpub = max(kpub, min(max(e - 15, 0), 100));
-    kst_exp[st] = kpub;
-    lstore(stage, true, __builtin_ldexpf(1.f, -kpub));
-  };
-  // Brings the accumulator to the scale of the tile about to be used.
-  auto align_scale = [&](int st) {
-    if (kst_exp[st] > kexp) {
-      const float corr = __builtin_ldexpf(1.f, kexp - kst_exp[st]);
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
-      kexp = kst_exp[st];
-    }
-  };
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
+  float m_run = -1e30f;
+  float l_run = 0.f;
+  int kexp = 0;  // o counts in units of 2^kexp
 
   // ---- one 32-key chunk: scores S^T (MFMA), online softmax, P in fp16,
-  // O^T += V^T P^T (MFMA).
-  auto scores = [&](const char* k_lds, int j, f32x16_t& sacc) {
+  // O^T += V^T P^T (MFMA).  Lane (h, r) of the K operand reads key pi(r).
+  const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+  auto scores = [&](const char* st, int j, f32x16_t& sacc) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    const char* krow = k_lds + (32 * j + r) * S::KROW + h * 16;
+    // block 2j + (r >= 16), token pi(r) % 16, d-granule 2 ks + h
+    const char* kp = st + (2 * j + (r >> 4)) * S::TILE + (h * 16 + (pr & 15)) * 16;
+    // all fragments first (the scheduler would otherwise pair each read
+    // with its MFMA and expose the LDS latency eight times)
+    uint4 a[S::KS];
 #pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const uint4 a = *reinterpret_cast<const uint4*>(krow + ks * 32);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks], sacc,
+    for (int ks = 0; ks < S::KS; ++ks) a[ks] = *reinterpret_cast<const uint4*>(kp + ks * 512);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks]), qb[ks], sacc,
                                                      0, 0, 0);
-    }
   };
-  // Lane (h, r) holds S^T[key kj + 8 (i / 4) + 4 h + i % 4][row r], i < 16.
-  auto softmax_pv = [&](const char* k_lds, int k0, int j, f32x16_t& sacc) {
-    const char* v_lds = k_lds + S::KT * S::KROW;
+  // Lane (h, r) holds S^T for keys kj + 16 (i / 8) + 8 h + (i % 8), i < 16.
+  auto softmax_pv = [&](const char* st, i32x4_t ex, int k0, int j, f32x16_t& sacc) {
     const int kj = k0 + 32 * j;
-    if (__builtin_expect(kj + 31 > wp0, 0)) {  // wave-uniform: the chunk reaches the diagonal
-      const int kl = lim - (kj + 4 * h);  // key offsets in the chunk up to kl are visible
+    // V^T fragments of both 16-key blocks, read before the softmax so their
+    // LDS latency is hidden behind it: block 2j + kk, granule (key group h,
+    // d = 32 db + r)
+    f16x8_t va[2][S::DB];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = (8 * (i >> 2) + (i & 3) <= kl) ? sacc[i] : -INFINITY;
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* vp = st + (4 + 2 * j + kk) * S::TILE + (h * D + r) * 16;
+#pragma unroll
+      for (int db = 0; db < S::DB; ++db)
+        va[kk][db] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(vp + db * 512));
     }
-    float mt = fmaxf(fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3])),
-                     fmaxf(fmaxf(sacc[4], sacc[5]), fmaxf(sacc[6], sacc[7])));
-    mt = fmaxf(mt, fmaxf(fmaxf(fmaxf(sacc[8], sacc[9]), fmaxf(sacc[10], sacc[11])),
-                         fmaxf(fmaxf(sacc[12], sacc[13]), fmaxf(sacc[14], sacc[15]))));
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_expect(kj + 31 > wp0, 0)) {  // wave-uniform: the chunk reaches the diagonal
+      const int kl = lim - (kj + 8 * h);  // offsets i' = 16 (i / 8) + i % 8 up to kl are visible
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = (16 * (i >> 3) + (i & 7) <= kl) ? sacc[i] : -INFINITY;
+    }
+    float mt = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0], sacc[1]),
+                                      __builtin_elementwise_maximum(sacc[2], sacc[3])),
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[4], sacc[5]),
+                                      __builtin_elementwise_maximum(sacc[6], sacc[7])));
+    mt = __builtin_elementwise_maximum(
+        mt, __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[8], sacc[9]),
+                                              __builtin_elementwise_maximum(sacc[10], sacc[11])),
+                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[12], sacc[13]),
+                                              __builtin_elementwise_maximum(sacc[14], sacc[15]))));
     mt = half_swap_max(mt) * c;
     const bool need = mt > m_run + kRescaleSlack;
     if (__ballot(need)) {
@@ -1102,73 +1103,57 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
                          __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w + 1], c, nm)));
       l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[w]), one, l_run, false);
     }
+    const int ekk[2] = {j ? ex.z : ex.x, j ? ex.w : ex.y};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      const int e = ekk[kk];
+      if (__builtin_expect(e != kexp, 0)) {  // uniform; only with some |v| >= 2^16
+        if (e > kexp) {
+          const float corr = __builtin_ldexpf(1.f, kexp - e);
+#pragma unroll
+          for (int db = 0; db < S::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[db][i] *= corr;
+          kexp = e;
+        } else {
+          const _Float16 f = (_Float16)__builtin_ldexpf(1.f, e - kexp);
+          const f16x2_t f2 = {f, f};
+#pragma unroll
+          for (int w = 4 * kk; w < 4 * kk + 4; ++w)
+            pk[w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pk[w]) * f2);
+        }
+      }
       const f16x8_t bop = __builtin_bit_cast(
           f16x8_t, make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
-      f16x8_t a[S::DB];
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
-        a[db] = __builtin_bit_cast(
-            f16x8_t, *reinterpret_cast<const uint4*>(v_lds + (32 * db + r) * S::VROW +
-                                                      (2 * j + kk) * 32 + h * 16));
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[db], bop, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kk][db], bop, o[db], 0, 0, 0);
     }
   };
 
-  // Pass 0 runs unguarded; pass 1 (guarded) only if some output of pass 0
-  // came out non-finite, which a V value of magnitude >= 2^16 causes.
-  for (int pass = 0; pass < 2; ++pass) {
-    const bool guarded = pass == 1;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-    // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
-    m_run = -1e30f;
-    l_run = 0.f;
-    kexp = 0;
-    kpub = 0;
-    kst_exp[0] = kst_exp[1] = 0;
-
-    load_ids(0);
-    gload(0);
-    publish(0, 0, guarded);
-    if (nkt > 1) gload(1);
-    __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < nkt) publish(kt + 1, st ^ 1, guarded);  // its stage was freed last barrier
-      if (kt + 2 < nkt) gload(kt + 2);                     // in flight while this tile is computed
-      const int k0 = kt * S::KT;
-      if (k0 <= wlast) {
-        const char* stage = lds + st * S::STAGE;
-        if (guarded) align_scale(st);
-        // both chunks' scores first, so the softmax of chunk 0 overlaps the
-        // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
-        const bool two = k0 + 32 <= wlast;
-        f32x16_t s0, s1;
-        scores(stage, 0, s0);
-        if (two) scores(stage, 1, s1);
-        softmax_pv(stage, k0, 0, s0);
-        if (two) softmax_pv(stage, k0, 1, s1);
-      }
-      __syncthreads();  // tile kt + 1 is stored; every wave is done with tile kt
+  // vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding)
+  constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
+  auto step = [&](int kt, const char* cur, char* nxt) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile kt have landed
+    __syncthreads();                       // everyone's have; `nxt` is free again
+    if (kt + 1 < nkt) issue(kt + 1, nxt);
+    const int k0 = kt * S::KT;
+    if (k0 <= wlast) {
+      const i32x4_t ex = vexp4[kt];
+      // both chunks' scores first, so the softmax of chunk 0 overlaps the
+      // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
+      const bool two = k0 + 32 <= wlast;
+      f32x16_t s0, s1;
+      scores(cur, 0, s0);
+      if (two) scores(cur, 1, s1);
+      softmax_pv(cur, ex, k0, 0, s0);
+      if (two) softmax_pv(cur, ex, k0, 1, s1);
     }
-    if (guarded) break;
-    float sum = 0.f;
-#pragma unroll
-    for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sum += o[db][i];
-    const bool bad = __ballot(row_ok && !__builtin_isfinite(sum)) != 0;
-    if (lane == 0) flag_lds[4 + wave] = bad ? 1.f : 0.f;
-    __syncthreads();
-    const float4 fl = *reinterpret_cast<const float4*>(flag_lds + 4);
-    if (fl.x + fl.y + fl.z + fl.w == 0.f) break;
-    __syncthreads();  // every wave has read the flags and left the last tile
+  };
+  issue(0, lds0);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(kt, lds0, lds1);
+    if (kt + 1 < nkt) step(kt + 1, lds1, lds0);
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -1191,8 +1176,9 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_tile(
     PrefillParams p) {
-  __shared__ __align__(16) char lds[PrefillLds<D, G>::BYTES];
-  prefill_item<D, G>(p, blockIdx.x, lds);
+  __shared__ __align__(16) char lds0[PrefillLds<D, G>::STAGE];
+  __shared__ __align__(16) char lds1[PrefillLds<D, G>::STAGE];
+  prefill_item<D, G>(p, blockIdx.x, lds0, lds1);
 }
 
 // One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
@@ -1208,19 +1194,29 @@ struct MixedParams {
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mixed(MixedParams m) {
   constexpr int DEC = DecodeLds<2, D, G>::BYTES;
-  constexpr int PRE = PrefillLds<D, G>::BYTES;
-  __shared__ __align__(16) char lds[PRE > 4 * DEC ? PRE : 4 * DEC];
+  constexpr int PRE = PrefillLds<D, G>::STAGE;
+  static_assert(4 * DEC <= PRE, "decode waves share the first prefill stage");
+  __shared__ __align__(16) char lds0[PRE];
+  __shared__ __align__(16) char lds1[PRE];
   if ((int)blockIdx.x < m.n_prefill) {
-    prefill_item<D, G>(m.pp, blockIdx.x, lds);
+    prefill_item<D, G>(m.pp, blockIdx.x, lds0, lds1);
   } else {
     const int wave = threadIdx.x >> 6;
     const int item = ((int)blockIdx.x - m.n_prefill) * 4 + wave;
-    decode_item<2, D, G>(m.dp, item, lds + wave * DEC);
+    decode_item<2, D, G>(m.dp, item, lds0 + wave * DEC);
   }
 }
 
 template <int D>
+static hipError_t v_fp16(const PrefillParams& p, hipStream_t stream) {
+  const int64_t items = p.vblocks * p.hkv;
+  hipLaunchKernelGGL((k_v_fp16<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
 static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
+  if (hipError_t e = v_fp16<D>(p, stream)) return e;
   switch (G) {
     case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
@@ -1243,6 +1239,9 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
   p.qsl = a.query_start_loc;
   p.num_seqs = a.num_seqs;
   p.scale_log2 = a.scale * kLog2e;
+  p.vh = a.ws_v;
+  p.vexp = a.ws_vexp;
+  p.vblocks = a.prefill_vblocks;
   return p;
 }
 
@@ -1260,6 +1259,7 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
 template <int D, int G>
 static hipError_t mixed_t(const MixedParams& m, int64_t grid, int num_seqs, int hkv,
                           hipStream_t stream) {
+  if (hipError_t e = v_fp16<D>(m.pp, stream)) return e;
   hipLaunchKernelGGL((k_mixed<D, G>), dim3((unsigned)grid), dim3(256), 0, stream, m);
   hipLaunchKernelGGL((k_decode_merge<D, G>), dim3((unsigned)((int64_t)num_seqs * hkv)),
                      dim3(64 * (G < 4 ? G : 4)), 0, stream, m.dp);

@@ -183,3 +183,42 @@ def test_many_sequences_and_long_rows():
     want = np.concatenate([scenario.sequence_attention(w, s) for s in rows])
     got = np.concatenate([out[s:s + 1] for s in rows])
     _check_attention(got, want, "bf16", "many sequences")
+
+
+def _times_pow2(codes: np.ndarray, k: int) -> np.ndarray:
+    """bf16 codes times 2^k, exactly (exponent field + k; zeros stay zero)."""
+    out = codes.copy()
+    nz = (out & 0x7F80) != 0
+    out[nz] = out[nz] + np.uint16(k << 7)
+    return out
+
+
+def test_prefill_values_beyond_fp16_range():
+    """V values of magnitude >= 2^16 in some blocks of a prefill sequence: the
+    prefill path's power-of-two block scaling (both directions) against the
+    oracle.  The absolute bar scales with the output's magnitude here."""
+    w = workloads.small(4)
+    s = w.batch - 1                                   # the prefill chunk
+    a, b = int(w.hist_start[s]), int(w.hist_start[s + 1])
+    hv = w.hist_v.copy()
+    hv[a + 3:a + 9] = _times_pow2(hv[a + 3:a + 9], 22)      # ~4e6 in block 0
+    hv[a + 20:a + 30] = _times_pow2(hv[a + 20:a + 30], 12)  # ~4e3, below 2^16
+    w.hist_v = hv
+    nv = w.new_v.copy()
+    q0 = int(w.query_start_loc[s])
+    nv[q0 + 60:q0 + 64] = _times_pow2(nv[q0 + 60:q0 + 64], 30)  # ~1e9 later on
+    nv[q0 + 100:q0 + 101] = _times_pow2(nv[q0 + 100:q0 + 101], 17)
+    w.new_v = nv
+    _announce(f"prefill with |v| >= 2^16: L={int(w.seq_lens[s])} q_len={int(w.q_len[s])}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)["out"]
+    got = st.out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    rows = slice(int(w.query_start_loc[s]), int(w.query_start_loc[s + 1]))
+    for name, sl in (("prefill rows", rows), ("decode rows", slice(0, rows.start))):
+        g, r = got[sl], ref[sl]
+        scale = max(float(np.abs(r).max()), 1.0)
+        max_abs = float(np.abs(g - r).max())
+        rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+        assert max_abs <= MAX_ABS_BF16 * scale, f"{name}: max|d| {max_abs:.3e} (scale {scale:.3e})"
+        assert rel <= REL_L2_BF16, f"{name}: rel L2 {rel:.3e}"

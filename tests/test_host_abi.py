@@ -160,9 +160,15 @@ def test_workspace_sizing():
     header = 256                                      # workspace header
     assert P.pkv_attention_workspace_bytes(cache, 32, lens) == header + units * 32 * (128 + 2) * 4
     qsl = np.array([0, 1, 2, 3, 3, 1000], np.int32)   # seq 4 is a prefill chunk
-    assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == header + 4 * 32 * 130 * 4
+    # a prefill sequence of length L adds fp16 V tiles of its blocks, rounded
+    # up to whole 64-key tiles, for every kv head, and one int32 exponent each
+    vblocks = 4 * -(-8192 // 64)
+    prefill = vblocks * 8 * (16 * 128 * 2 + 4)
+    dec = header + 4 * 32 * 130 * 4
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == -(-dec // 256) * 256 + prefill
     only_prefill = np.array([0, 1000], np.int32)
-    assert P.pkv_attention_workspace_bytes(cache, 32, lens[4:], only_prefill) == 0
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens[4:], only_prefill) == header + prefill
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens[3:4], np.array([0, 0], np.int32)) == 0
 
 
 def _call_decode(cache_desc, out=1, q=1, bt=1, sl=1, h_sl=None, n=1, hq=32, ws=None, ws_bytes=0,
