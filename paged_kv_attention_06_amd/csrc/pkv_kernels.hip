@@ -762,10 +762,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-// Scalar-cache view of read-only device arrays whose index is wave-uniform.
-typedef const __attribute__((address_space(4))) int32_t sint32_t;
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-typedef const __attribute__((address_space(4))) i32x4_t sint4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct PrefillParams {
@@ -996,21 +993,33 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 
   const int nkt = (pend + S::KT - 1) / S::KT;      // key tiles needed (keys < pend)
   const int nbl = (L + BS - 1) / BS;               // valid block-table entries
-  sint32_t* bt = (sint32_t*)(p.block_tables + (size_t)s * p.max_blocks);
   const char* k_src = p.kv + (size_t)kvh * 2 * S::TILE + lane * 16;
   const char* v_src = p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
-  sint4_t* vexp4 = (sint4_t*)(p.vexp + (size_t)kvh * p.vblocks + vbase);
 
-  // ---- wave w copies block w of a tile: its K tile from the pool (blocks
-  // past the table are left stale: their keys are masked) and its fp16 V
-  // tile from the workspace (zero there past L).
-  int id_next = wave < nbl ? bt[wave] : 0;  // block id for the next copy
+  // Per-tile metadata travels in one vector load issued with the copies of
+  // the tile before (scalar loads would make every later LDS wait also wait
+  // for them): lanes 0..3 get the block ids of tile t, lanes 4..7 the V
+  // exponents of tile t - 1.
+  const int32_t* bt_row = p.block_tables + (size_t)s * p.max_blocks;
+  const int32_t* exp_row = p.vexp + (size_t)kvh * p.vblocks + vbase;
+  int meta = 0;
+  auto load_meta = [&](int t) {
+    const int i = lane & 3;
+    const int32_t* src = lane < 4 ? bt_row + min(t * 4 + i, nbl - 1)
+                                  : exp_row + max(t - 1, 0) * 4 + i;
+    meta = *src;
+  };
+
+  // ---- wave w copies block w of tile kt (ids in `meta`): its K tile from
+  // the pool (blocks past the table are left stale: their keys are masked)
+  // and its fp16 V tile from the workspace (zero there past L).
   auto issue = [&](int kt, char* stage) {
     char* kd = stage + wave * S::TILE;
     char* vd = kd + 4 * S::TILE;
     const int blk = kt * 4 + wave;
     if (blk < nbl) {
-      const char* ks = k_src + (size_t)id_next * p.block_bytes;
+      const int id = __builtin_amdgcn_readlane(meta, wave);
+      const char* ks = k_src + (size_t)id * p.block_bytes;
 #pragma unroll
       for (int i = 0; i < S::CP; ++i)
         __builtin_amdgcn_global_load_lds(ks + i * 1024, (lds_void_t*)(kd + i * 1024), 16, 0, 0);
@@ -1019,7 +1028,6 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 #pragma unroll
     for (int i = 0; i < S::CP; ++i)
       __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
-    id_next = blk + 4 < nbl ? bt[blk + 4] : 0;
   };
 
   f32x16_t o[S::DB];
@@ -1136,10 +1144,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   auto step = [&](int kt, const char* cur, char* nxt) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile kt have landed
     __syncthreads();                       // everyone's have; `nxt` is free again
+    const i32x4_t ex = {__builtin_amdgcn_readlane(meta, 4), __builtin_amdgcn_readlane(meta, 5),
+                        __builtin_amdgcn_readlane(meta, 6), __builtin_amdgcn_readlane(meta, 7)};
     if (kt + 1 < nkt) issue(kt + 1, nxt);
+    load_meta(kt + 2);
     const int k0 = kt * S::KT;
     if (k0 <= wlast) {
-      const i32x4_t ex = vexp4[kt];
       // both chunks' scores first, so the softmax of chunk 0 overlaps the
       // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
       const bool two = k0 + 32 <= wlast;
@@ -1150,7 +1160,10 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
       if (two) softmax_pv(cur, ex, k0, 1, s1);
     }
   };
+  load_meta(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   issue(0, lds0);
+  load_meta(1);
   for (int kt = 0; kt < nkt; kt += 2) {
     step(kt, lds0, lds1);
     if (kt + 1 < nkt) step(kt + 1, lds1, lds0);
