@@ -1,7 +1,10 @@
 // Host side of the C ABI declared in include/pkv.h: argument checks, work
 // sizing, launches, the slot-mapping builder and the block allocator.
+#include <atomic>
+#include <chrono>
 #include <climits>
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <deque>
@@ -74,6 +77,8 @@ struct Plan {
   int prefill_seqs = 0;
   int64_t prefill_vblocks = 0;
   int64_t num_tokens = 0;
+  int64_t stream_steps = 0;  // per kv head: sum over decode rows of steps + setup charge
+  int32_t num_seqs = 0;
 };
 
 // Validates host lengths and counts the work.  qsl may be NULL (decode).
@@ -96,6 +101,7 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
                   (long long)ql, (long long)L);
     if (ql == 1) {
       if (L > 0) {
+        plan->stream_steps += (L + 31) / 32 + pkv::kStreamSetupCost;
         plan->decode_units += (L + pkv::kPartTokens - 1) / pkv::kPartTokens;
         plan->full_units += L / pkv::kPartTokens;
         const int64_t rem = L % pkv::kPartTokens;
@@ -109,17 +115,55 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
     }
     plan->num_tokens += ql;
   }
+  plan->num_seqs = num_seqs;
   return PKV_OK;
+}
+
+// Stream decode sizing: total cost and the most waves a call may use.
+int64_t stream_total(const Plan& p, int hkv) { return p.stream_steps * hkv; }
+int64_t stream_wave_cap(const Plan& p, int hkv) {
+  const int64_t t = stream_total(p, hkv);
+  const int64_t w = (t + pkv::kStreamMinCost - 1) / pkv::kStreamMinCost;
+  return w < pkv::kMaxStreamWaves ? w : pkv::kMaxStreamWaves;
+}
+
+// Epochs of stream-decode counters start at a value that differs between
+// runs, so counters left in a reused buffer by another process are stale.
+unsigned first_epoch() {
+  const auto t = std::chrono::steady_clock::now().time_since_epoch().count();
+  return (unsigned)t ^ (unsigned)((unsigned long long)t >> 32) ^ 0x9E3779B9u;
+}
+
+// Decode rows without prefill rows use the stream kernel unless
+// PKV_DECODE_SPLIT=units asks for fixed 256-token partitions plus a merge
+// launch (the path mixed batches use).
+bool stream_decode_enabled() {
+  const char* e = std::getenv("PKV_DECODE_SPLIT");
+  return !(e && std::strcmp(e, "units") == 0);
 }
 
 // Workspace layout: header | decode partials acc [units][hq][D], (m, l)
 // [units][hq][2] | (256-aligned) fp16 V tiles [vblocks][hkv][16 D] | their
-// exponents [hkv][vblocks].
+// exponents [hkv][vblocks].  A call without prefill rows may instead run the
+// stream kernel: header | partials acc [2 waves][G][D], (m, l) [2 waves][G][2]
+// | (256-aligned) counters [num_seqs][hkv] (8 bytes each); it is given the
+// larger of the two sizes.
 struct WsLayout {
   size_t v_off, exp_off, total;
+  size_t st_ml_off, st_ctr_off;  // stream layout (offsets from the start)
 };
 WsLayout ws_layout(const Plan& p, int hq, int hkv, int D) {
-  WsLayout w{0, 0, 0};
+  WsLayout w{0, 0, 0, 0, 0};
+  if (p.decode_units > 0 && p.prefill_tiles == 0) {
+    const int G = hq / hkv;
+    const size_t wc = (size_t)stream_wave_cap(p, hkv);
+    w.st_ml_off = pkv::kWorkspaceHeader + 2 * wc * G * D * sizeof(float);
+    w.st_ctr_off = (w.st_ml_off + 2 * wc * G * 2 * sizeof(float) + 255) / 256 * 256;
+    const size_t st_total = w.st_ctr_off + (size_t)p.num_seqs * hkv * 8;
+    const size_t units = pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+    w.total = st_total > units ? st_total : units;
+    return w;
+  }
   if (p.decode_units == 0 && p.prefill_vblocks == 0) return w;
   const size_t dec = (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
   w.v_off = (pkv::kWorkspaceHeader + dec + 255) / 256 * 256;
@@ -184,6 +228,27 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.prefill_vblocks = plan.prefill_vblocks;
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
+  a.stream_waves = 0;
+  if (plan.prefill_tiles == 0 && plan.decode_units > 0 && stream_decode_enabled()) {
+    const int G = num_q_heads / c.hkv;
+    const int slots = pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
+    int64_t waves = stream_wave_cap(plan, c.hkv);
+    if (slots > 0 && slots < waves) waves = slots;
+    if (const char* e = std::getenv("PKV_STREAM_WAVES")) {  // tuning: cap the waves
+      const long long cap = std::atoll(e);
+      if (cap > 0 && cap < waves) waves = cap;
+    }
+    if (slots > 0) {
+      static std::atomic<unsigned> epoch{first_epoch()};
+      a.stream_total = stream_total(plan, c.hkv);
+      a.stream_waves = (int)waves;
+      a.stream_c0 = pkv::kStreamSetupCost;
+      a.stream_epoch = epoch.fetch_add(1, std::memory_order_relaxed);
+      a.stream_acc = reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader);
+      a.stream_ml = reinterpret_cast<float*>(ws + wl.st_ml_off);
+      a.stream_counters = reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off);
+    }
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.prefill_tiles > 0 && plan.decode_units > 0)
     return hip_status(pkv::launch_mixed_rows(c, a, st), "mixed rows");

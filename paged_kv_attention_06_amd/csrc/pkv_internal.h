@@ -16,6 +16,12 @@ constexpr int kPartTokens = 256;
 constexpr int prefill_tile_q(int g) { return 128 / g; }
 // Size classes of the short last partitions (by 32-token steps).
 constexpr int kPartClasses = kPartTokens / 32;
+// Stream decode: setup charge of an item in 32-token steps, the least cost
+// one wave's range is given, and the most waves one call may use (the
+// workspace holds two partials per wave).
+constexpr int kStreamSetupCost = 1;
+constexpr int kStreamMinCost = 8;
+constexpr int kMaxStreamWaves = 4096;
 // Bytes at the start of the attention workspace before the partials.
 constexpr size_t kWorkspaceHeader = 256;
 // Blocks of a prefill sequence of length L whose V the prefill path converts
@@ -51,6 +57,14 @@ struct AttnDesc {
   int64_t prefill_vblocks;         // blocks of the prefill sequences, each rounded up to 4
   char* ws_v;                      // fp16 V tiles of those blocks [vblock][hkv][16 * D]
   int32_t* ws_vexp;                // their power-of-two scale exponents [hkv][vblock]
+  // stream decode (stream_waves > 0 selects it)
+  int64_t stream_total;            // cost of all (row, kv head) items
+  int stream_waves;                // ranges / waves of the launch
+  int stream_c0;                   // setup charge per item
+  unsigned stream_epoch;           // distinct per call
+  unsigned long long* stream_counters;  // [num_seqs][hkv]
+  float* stream_acc;               // [2 * waves][G][D]
+  float* stream_ml;                // [2 * waves][G][2]
 };
 
 hipError_t launch_kv_write(const CacheDesc& c, const void* k_new, const void* v_new,
@@ -67,6 +81,9 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
 hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 
 bool supported_group(int g);
+// Waves of the stream decode kernel the current device holds at once (0 if
+// it cannot be queried).
+int decode_stream_slots(int dtype_bytes, int D, int G);
 // Group sizes the mixed path's prefill rows support (bf16 caches only).
 inline bool prefill_supported(int g, int dtype_bytes) {
   return dtype_bytes == 2 && (g == 1 || g == 2 || g == 4);

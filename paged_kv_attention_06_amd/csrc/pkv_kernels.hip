@@ -70,6 +70,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform64(long long v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
 
 // Orders one wave's LDS writes before its later LDS reads by other lanes.
 // A wave's LDS operations execute in issue order, so keeping the compiler
@@ -661,6 +666,595 @@ __global__ __launch_bounds__(256) void k_decode_merge(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Stream decode (calls without prefill rows).  The decode work is laid out
+// on one line of cost: item (row s, kv head h), h fastest, costs a setup
+// charge c0 followed by one unit per 32-token step of the row.  The line is
+// cut into `waves` equal ranges, one per wave, and the grid is sized to the
+// waves the GPU holds at once, so every wave streams the same number of
+// steps and all finish together: there is no tail of short units.
+//
+// A wave walks its range step by step.  Its pipeline runs two steps ahead:
+// while step k is computed the K/V of step k + 1 are in flight, and the
+// block ids of step k + 2 travel in one small vector load issued with them
+// (as do the q rows of an item that starts at step k + 1), so waiting for a
+// step's data also covers its metadata and item changes cost no bubble.
+//
+// An item whose steps fall in one wave's range is finished there.  An item
+// split over waves wA..wB leaves one partial (max, sum, weighted V) per wave
+// in the workspace; each contributor then counts itself in the item's
+// counter, and the last one merges the partials into the output row, so no
+// second launch is needed.  Counters carry the call's epoch in their upper
+// half: a counter whose epoch differs is stale and counts as zero, so the
+// workspace needs no clearing between calls.
+// ---------------------------------------------------------------------------
+// Partials travel between waves that may sit on different XCDs, whose L2
+// caches are not coherent with each other.  They are written and read with
+// agent-scope relaxed atomics (coherent at the device level, instruction by
+// instruction); a writer waits until its stores are complete before it
+// counts itself in, and the merging wave reads the partials only after its
+// count, so no fence has to write back or invalidate a whole L2.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() {
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+struct StreamParams {
+  DecodeParams d;
+  long long total;               // cost of all items
+  int waves;                     // ranges = grid size
+  int c0;                        // setup charge per item, in steps
+  unsigned epoch;                // distinct per call
+  unsigned long long* counters;  // [num_seqs][hkv]
+  float* part_acc;               // [2 * waves][G][D]
+  float* part_ml;                // [2 * waves][G][2]
+};
+
+// One (item, step) position of a wave's walk.  All fields are wave-uniform.
+struct StreamCur {
+  int valid;
+  int s, h, j;  // sequence, kv head, step within the item
+  int n, L;     // steps and tokens of the sequence
+  int row;      // output row of the sequence
+  long long A;  // cost position of step 0 of the item
+};
+
+// Wave whose range holds cost position t: the largest w with
+// floor(w * T / W) <= t.
+__device__ __forceinline__ int stream_wave_of(long long t, long long T, int W) {
+  return (int)(((t + 1) * (long long)W - 1) / T);
+}
+
+template <int ES, int D, int G>
+struct StreamLds {
+  static constexpr int QBUF = G * 2 * DecodeShape<ES, D>::QROW;
+};
+
+template <int ES, int D, int G>
+__device__ __forceinline__ void stream_merge(const StreamParams& sp, int wA, int wB, float* o) {
+  // o: the G output rows of the item (query heads kvh * G .. + G - 1)
+  constexpr int DPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nw = wB - wA + 1;
+  auto slot_of = [wA](int w) { return 2 * w + (w == wA ? 1 : 0); };
+  if (nw <= 8) {
+    // every load first (contributors past nw repeat the last one and get
+    // weight 0), then the arithmetic: one round trip to memory
+    constexpr int K = 8;
+    float m[G], l[G], a[G][K][DPL];
+    const int my = slot_of(wA + min(lane, nw - 1));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = load_agent(sp.part_ml + ((size_t)my * G + g) * 2);
+      l[g] = load_agent(sp.part_ml + ((size_t)my * G + g) * 2 + 1);
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const int sk = slot_of(wA + min(k, nw - 1));
+#pragma unroll
+        for (int j = 0; j < DPL; ++j)
+          a[g][k][j] = load_agent(sp.part_acc + ((size_t)sk * G + g) * D + j * 64 + lane);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float M = wave_max(lane < nw ? m[g] : -INFINITY);
+      const float wq = lane < nw ? __builtin_amdgcn_exp2f(m[g] - M) : 0.f;
+      const float den = wave_sum(wq * l[g]);
+      float num[DPL];
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) num[j] = 0.f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), k));
+#pragma unroll
+        for (int j = 0; j < DPL; ++j) num[j] = fmaf(wk, a[g][k][j], num[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+    }
+    return;
+  }
+  for (int g = 0; g < G; ++g) {
+    float M = -INFINITY;
+    for (int c = 0; c < nw; c += 64) {
+      const int w = wA + c + lane;
+      if (c + lane < nw) {
+        const int slot = 2 * w + (w == wA ? 1 : 0);
+        M = fmaxf(M, load_agent(sp.part_ml + ((size_t)slot * G + g) * 2));
+      }
+    }
+    M = wave_max(M);
+    float den = 0.f, num[DPL];
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) num[j] = 0.f;
+    for (int c = 0; c < nw; c += 64) {
+      const int w = wA + c + lane;
+      float wq = 0.f;
+      if (c + lane < nw) {
+        const int slot = 2 * w + (w == wA ? 1 : 0);
+        const float* ml = sp.part_ml + ((size_t)slot * G + g) * 2;
+        wq = __builtin_amdgcn_exp2f(load_agent(ml) - M);
+        den = fmaf(wq, load_agent(ml + 1), den);
+      }
+      const int n = min(64, nw - c);
+      int i = 0;
+      for (; i + 4 <= n; i += 4) {
+        float a[4][DPL];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int w2 = wA + c + i + k;
+          const int slot = 2 * w2 + (w2 == wA ? 1 : 0);
+#pragma unroll
+          for (int j = 0; j < DPL; ++j)
+            a[k][j] = load_agent(sp.part_acc + ((size_t)slot * G + g) * D + j * 64 + lane);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), i + k));
+#pragma unroll
+          for (int j = 0; j < DPL; ++j) num[j] = fmaf(wk, a[k][j], num[j]);
+        }
+      }
+      for (; i < n; ++i) {
+        const int w2 = wA + c + i;
+        const int slot = 2 * w2 + (w2 == wA ? 1 : 0);
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq), i));
+#pragma unroll
+        for (int j = 0; j < DPL; ++j)
+          num[j] = fmaf(wk, load_agent(sp.part_acc + ((size_t)slot * G + g) * D + j * 64 + lane), num[j]);
+      }
+    }
+    den = wave_sum(den);
+#pragma unroll
+    for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+  }
+}
+
+template <int ES, int D, int G>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_stream(
+    StreamParams sp) {
+  using S = DecodeShape<ES, D>;
+  constexpr int QBUF = StreamLds<ES, D, G>::QBUF;
+  constexpr int QGR = G * S::KG;             // 16-byte granules of one item's q rows
+  constexpr int NQ = (QGR + 63) / 64;        // per lane
+  __shared__ __align__(16) char q_lds[QBUF];
+  __shared__ __align__(16) float p_lds[32 * G];
+  __shared__ int len_lds[256];
+  __shared__ int row_lds[256];
+
+  const DecodeParams& p = sp.d;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x;
+  const int W = sp.waves;
+  const long long T = sp.total;
+  const int hkv = p.hkv;
+  const int hq = hkv * G;
+  const int c0 = sp.c0;
+
+  // ---- empty decode rows get zeros: sequences w, w + W, w + 2W, ...
+  for (long long sb = w; sb < p.num_seqs; sb += 64LL * W) {
+    const long long s = sb + (long long)lane * W;
+    bool zero = false;
+    if (s < p.num_seqs) {
+      const int ql = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
+      zero = ql == 1 && p.seq_lens[s] <= 0;
+    }
+    unsigned long long m = __ballot(zero);
+    while (m) {
+      const int l = __ffsll(m) - 1;
+      m &= m - 1;
+      const long long sz = sb + (long long)l * W;
+      const int row = p.qsl ? p.qsl[sz] : (int)sz;
+      float* o = p.out + (size_t)row * hq * D;
+      for (int i = lane; i < hq * D; i += 64) o[i] = 0.f;
+    }
+  }
+
+  const long long cs = (long long)w * T / W;
+  const long long ce = (long long)(w + 1) * T / W;
+  if (cs >= ce) return;
+
+  // ---- find the sequence whose cost range holds cs; keep its chunk of 256
+  // decode lengths (and output rows) in LDS for the walk
+  int s0 = 0;
+  long long base = 0;  // cost before sequence s0
+  auto cost_of = [&](int L) -> long long {
+    return L > 0 ? (long long)hkv * ((L + 31) / 32 + c0) : 0;
+  };
+  auto load_chunk = [&](int first) {
+    for (int k = 0; k < 4; ++k) {
+      const int s = first + 4 * lane + k;
+      len_lds[4 * lane + k] = s < p.num_seqs ? row_len(p.seq_lens, p.qsl, s) : 0;
+      row_lds[4 * lane + k] = s < p.num_seqs ? (p.qsl ? p.qsl[s] : s) : 0;
+    }
+    wave_sync();
+  };
+  int s_found = -1;
+  long long S_found = 0;
+  for (s0 = 0; s0 < p.num_seqs; s0 += 256) {
+    int len[4];
+    long long c[4], tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = s0 + 4 * lane + k;
+      len[k] = s < p.num_seqs ? row_len(p.seq_lens, p.qsl, s) : 0;
+      c[k] = cost_of(len[k]);
+      tot += c[k];
+    }
+    long long incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(incl, off);
+      if (lane >= off) incl += t;
+    }
+    const long long total = uniform64(__shfl(incl, 63));
+    if (cs < base + total) {
+      const unsigned long long m = __ballot(base + incl > cs);
+      const int hit = __ffsll(m) - 1;
+      long long start = base + incl - tot;  // cost before this lane's first sequence
+      int kk = 3;
+      long long Sk = start;
+      bool found = false;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (!found && cs < start + c[k]) {
+          kk = k;
+          Sk = start;
+          found = true;
+        }
+        start += c[k];
+      }
+      s_found = uniform(__shfl(s0 + 4 * lane + kk, hit));
+      S_found = uniform64(__shfl(Sk, hit));
+      break;
+    }
+    base += total;
+  }
+  if (s_found < 0) return;
+  load_chunk(s0);
+
+  auto len_of = [&](int s) -> int {  // decode length of sequence s (chunk reloaded on demand)
+    if (s >= s0 + 256) {
+      s0 = s - (s - s0) % 256;
+      wave_sync();
+      load_chunk(s0);
+    }
+    return uniform(len_lds[s - s0]);
+  };
+  auto row_of = [&](int s) -> int { return uniform(row_lds[s - s0]); };
+
+  StreamCur cur0;
+  {
+    const int L = len_of(s_found);
+    const int n = (L + 31) / 32;
+    const long long h = (cs - S_found) / (n + c0);
+    cur0.s = s_found;
+    cur0.h = (int)h;
+    cur0.n = n;
+    cur0.L = L;
+    cur0.row = row_of(s_found);
+    cur0.A = S_found + h * (n + c0) + c0;
+    cur0.j = (int)max(0LL, cs - cur0.A);
+    cur0.valid = cur0.A + cur0.j < ce;
+  }
+  if (!cur0.valid) return;
+
+  auto next = [&](const StreamCur& c) {
+    StreamCur r = c;
+    if (!c.valid) return r;
+    if (c.j + 1 < c.n) {
+      r.j = c.j + 1;
+      r.valid = c.A + r.j < ce;
+      return r;
+    }
+    r.A = c.A + c.n + c0;
+    r.j = 0;
+    if (r.A >= ce) {
+      r.valid = 0;
+      return r;
+    }
+    if (c.h + 1 < hkv) {
+      r.h = c.h + 1;
+      return r;
+    }
+    int s = c.s + 1;
+    int L = 0;
+    while (s < p.num_seqs && (L = len_of(s)) <= 0) ++s;
+    if (s >= p.num_seqs) {
+      r.valid = 0;
+      return r;
+    }
+    r.s = s;
+    r.h = 0;
+    r.L = L;
+    r.n = (L + 31) / 32;
+    r.row = row_of(s);
+    return r;
+  };
+
+  // block ids of a step: lane l gets block 2j + (l & 1) of the item's row
+  auto load_ids = [&](const StreamCur& c) -> int {
+    const int nblk = (c.L + BS - 1) / BS;
+    const int b = min(2 * c.j + (lane & 1), nblk - 1);
+    return p.block_tables[(size_t)c.s * p.max_blocks + b];
+  };
+  auto load_q = [&](uint4 (&qr)[NQ], const StreamCur& c) {
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(p.q) + ((size_t)c.row * hq + (size_t)c.h * G) * D * ES);
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int gi = lane + 64 * i;
+      qr[i] = (gi < QGR) ? src[gi] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store_q = [&](const uint4 (&qr)[NQ]) {
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int gi = lane + 64 * i;
+      if (gi < QGR) {
+        const int g = gi / S::KG, c = gi % S::KG;
+        const int hh = c / S::KH, cc = c % S::KH;
+        *reinterpret_cast<uint4*>(q_lds + (g * 2 + hh) * S::QROW + cc * 16) = qr[i];
+      }
+    }
+  };
+
+  const int half = lane & 1;
+  const int t_in_blk = (lane >> 1) & 15;
+  const int bsel = lane >> 5;
+  const int k_lane_off = (half * S::KH * BS + t_in_blk) * 16;
+  auto load_kv = [&](StepRegs<ES, D>& r, int h, int b0, int b1) {
+    const char* head_base = p.kv + (size_t)h * 2 * S::TILE;
+    const char* base0 = head_base + (size_t)b0 * p.block_bytes;
+    const char* base1 = head_base + (size_t)b1 * p.block_bytes;
+    const char* kp = (bsel ? base1 : base0) + k_lane_off;
+#pragma unroll
+    for (int cc = 0; cc < S::KH; ++cc) r.k[cc] = *reinterpret_cast<const uint4*>(kp + cc * BS * 16);
+#pragma unroll
+    for (int i = 0; i < S::VG; ++i) {
+      r.v[0][i] = *reinterpret_cast<const uint4*>(base0 + S::TILE + i * 1024 + lane * 16);
+      r.v[1][i] = *reinterpret_cast<const uint4*>(base1 + S::TILE + i * 1024 + lane * 16);
+    }
+  };
+
+  float m_run[G], l_lane[G], acc[G][S::DPL];
+  auto reset_state = [&]() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_lane[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < S::DPL; ++j) acc[g][j] = 0.f;
+    }
+  };
+
+  auto compute = [&](const StepRegs<ES, D>& r, const StreamCur& c) {
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[g] = 0.f;
+    const char* qh = q_lds + half * S::QROW;
+    uint4 qcur[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qcur[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW);
+#pragma unroll
+    for (int cc = 0; cc < S::KH; ++cc) {
+      uint4 qnext[G];
+      const int cn = cc + 1 < S::KH ? cc + 1 : cc;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        qnext[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + cn * 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 qg = qcur[g];
+        const uint4 kg = r.k[cc];
+        if constexpr (ES == 2) {
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.x),
+                                                  __builtin_bit_cast(bf16x2_t, kg.x), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.y),
+                                                  __builtin_bit_cast(bf16x2_t, kg.y), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.z),
+                                                  __builtin_bit_cast(bf16x2_t, kg.z), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.w),
+                                                  __builtin_bit_cast(bf16x2_t, kg.w), sc[g], false);
+        } else {
+          sc[g] = fmaf(__uint_as_float(qg.x), __uint_as_float(kg.x), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.y), __uint_as_float(kg.y), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.z), __uint_as_float(kg.z), sc[g]);
+          sc[g] = fmaf(__uint_as_float(qg.w), __uint_as_float(kg.w), sc[g]);
+        }
+        qcur[g] = qnext[g];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
+    }
+    const int tok0 = c.j * 32;
+    const bool tok_ok = tok0 + (lane >> 1) < c.L;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float full = sc[g] + dpp_f<0xB1>(sc[g]);
+      const float x = tok_ok ? full * p.scale_log2 : -INFINITY;
+      const float mi = wave_max(x);
+      if (mi > m_run[g] + kRescaleSlack) {
+        const float corr = __builtin_amdgcn_exp2f(m_run[g] - mi);
+        l_lane[g] *= corr;
+#pragma unroll
+        for (int j = 0; j < S::DPL; ++j) acc[g][j] *= corr;
+        m_run[g] = mi;
+      }
+      const float pr = __builtin_amdgcn_exp2f(x - m_run[g]);
+      if (half == 0) {
+        l_lane[g] += pr;
+        p_lds[(lane >> 1) * G + g] = pr;
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) {
+      const int valid = c.L - (tok0 + jb * BS);
+      if (valid >= BS)
+        pv_block<ES, D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
+      else if (valid > 0)
+        pv_block<ES, D, G, true>(r.v[jb], p_lds, jb * BS, valid, acc);
+    }
+    wave_sync();
+  };
+
+  // Split items this wave has left a partial for.
+  struct Pending {
+    int ctr, wA, wB, row, h;
+  };
+  Pending pend0 = {0, 0, 0, 0, 0}, pend1 = {0, 0, 0, 0, 0};
+  int npend = 0;
+
+  // The item of `c` ends here (its last step in this wave's range).
+  auto finish = [&](const StreamCur& c) {
+    float l_tot[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_lane[g]);
+    const int wA = stream_wave_of(c.A, T, W);
+    const int wB = stream_wave_of(c.A + c.n - 1, T, W);
+    float* o = p.out + ((size_t)c.row * hq + (size_t)c.h * G) * D;
+    if (wA == wB) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < S::DPL; ++j) o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g];
+      reset_state();
+      return;
+    }
+    const int slot = 2 * w + (w == wA ? 1 : 0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < S::DPL; ++j)
+        store_agent(sp.part_acc + ((size_t)slot * G + g) * D + j * 64 + lane, acc[g][j]);
+      if (lane == 0) {
+        store_agent(sp.part_ml + ((size_t)slot * G + g) * 2, m_run[g]);
+        store_agent(sp.part_ml + ((size_t)slot * G + g) * 2 + 1, l_tot[g]);
+      }
+    }
+    reset_state();
+    // counted and merged after the walk (at most two split items per wave:
+    // the first and the last of its range)
+    if (npend == 0) {
+      pend0 = {c.s * hkv + c.h, wA, wB, c.row, c.h};
+    } else {
+      pend1 = {c.s * hkv + c.h, wA, wB, c.row, c.h};
+    }
+    ++npend;
+  };
+
+  // ---- the walk.  Two register sets alternate: ra holds the step being
+  // computed while rb receives the next one, then the roles swap.  Every
+  // step issues the same loads (the next step's K/V, the ids of the one
+  // after), so the compiler's wait counts stay exact on all paths: past the
+  // end of the range the ids come from the current step and the K/V are a
+  // re-read of the current step's blocks (an L2 hit).
+  StepRegs<ES, D> ra, rb;
+  uint4 qa[NQ], qb[NQ];
+  load_q(qa, cur0);
+  int ids_a = load_ids(cur0);  // ids of the step whose K/V go to ra
+  StreamCur cur1 = next(cur0);
+  int ids_b = load_ids(cur1.valid ? cur1 : cur0);
+  int lb0 = uniform(__builtin_amdgcn_readlane(ids_a, 0));  // blocks of the last K/V issued
+  int lb1 = uniform(__builtin_amdgcn_readlane(ids_a, 1));
+  load_kv(ra, cur0.h, lb0, lb1);
+  bool new0 = true;
+  reset_state();
+
+  // One step: compute `c` (data in rc, q rows in qc if it starts an item),
+  // with `cn` = the step after (K/V -> rn, q -> qn) and the step after that
+  // (its ids -> ids_out).
+  auto half_step = [&](StepRegs<ES, D>& rc, StepRegs<ES, D>& rn, uint4 (&qc)[NQ], uint4 (&qn)[NQ],
+                       const StreamCur& c, StreamCur& cn, int ids_n, int& ids_out, bool& new_c) {
+    StreamCur c2 = next(cn);
+    const bool new_n = cn.valid && (cn.s != c.s || cn.h != c.h);
+    if (new_n) load_q(qn, cn);
+    ids_out = load_ids(c2.valid ? c2 : c);
+    int hh = c.h;
+    if (cn.valid) {
+      lb0 = uniform(__builtin_amdgcn_readlane(ids_n, 0));
+      lb1 = uniform(__builtin_amdgcn_readlane(ids_n, 1));
+      hh = cn.h;
+    }
+    load_kv(rn, hh, lb0, lb1);
+    if (new_c) {
+      store_q(qc);
+      wave_sync();
+    }
+    compute(rc, c);
+    if (!cn.valid || new_n) finish(c);
+    new_c = new_n;
+    return c2;
+  };
+
+  for (;;) {
+    StreamCur c2 = half_step(ra, rb, qa, qb, cur0, cur1, ids_b, ids_a, new0);
+    if (!cur1.valid) break;
+    cur0 = cur1;
+    cur1 = c2;
+    // ids_a now holds the ids of cur1's step (K/V -> ra)
+    StreamCur c3 = half_step(rb, ra, qb, qa, cur0, cur1, ids_a, ids_b, new0);
+    if (!cur1.valid) break;
+    cur0 = cur1;
+    cur1 = c3;
+  }
+
+  // ---- count this wave into its split items (lanes 0 and 1 at once, after
+  // its partial stores are complete); the last contributor merges.
+  if (npend == 0) return;
+  wait_stores();
+  unsigned cnt = 0;
+  if (lane < npend) {
+    unsigned long long* ctr = sp.counters + (lane == 0 ? pend0.ctr : pend1.ctr);
+    const unsigned long long tag = (unsigned long long)sp.epoch << 32;
+    unsigned long long seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+      const unsigned long long want = ((seen >> 32) == sp.epoch) ? seen + 1 : (tag | 1ULL);
+      const unsigned long long prev = atomicCAS(ctr, seen, want);
+      if (prev == seen) {
+        cnt = (unsigned)want;
+        break;
+      }
+      seen = prev;
+    }
+  }
+  const unsigned cnt0 = (unsigned)__builtin_amdgcn_readlane((int)cnt, 0);
+  const unsigned cnt1 = (unsigned)__builtin_amdgcn_readlane((int)cnt, 1);
+  if (cnt0 == (unsigned)(pend0.wB - pend0.wA + 1))
+    stream_merge<ES, D, G>(sp, pend0.wA, pend0.wB,
+                           p.out + ((size_t)pend0.row * hq + (size_t)pend0.h * G) * D);
+  if (npend > 1 && cnt1 == (unsigned)(pend1.wB - pend1.wA + 1))
+    stream_merge<ES, D, G>(sp, pend1.wA, pend1.wB,
+                           p.out + ((size_t)pend1.row * hq + (size_t)pend1.h * G) * D);
+}
+
 template <int ES, int D, int G>
 static hipError_t decode_rows_t(const DecodeParams& p, int64_t units, int num_seqs, int hkv,
                                 hipStream_t stream) {
@@ -710,8 +1304,77 @@ static DecodeParams make_decode_params(const CacheDesc& c, const AttnDesc& a) {
   return p;
 }
 
+template <int ES, int D, int G>
+static hipError_t stream_t(const StreamParams& sp, hipStream_t stream) {
+  hipLaunchKernelGGL((k_decode_stream<ES, D, G>), dim3((unsigned)sp.waves), dim3(64), 0, stream, sp);
+  return hipGetLastError();
+}
+
+template <int ES, int D>
+static hipError_t stream_g(int G, const StreamParams& sp, hipStream_t stream) {
+  switch (G) {
+    case 1: return stream_t<ES, D, 1>(sp, stream);
+    case 2: return stream_t<ES, D, 2>(sp, stream);
+    case 4: return stream_t<ES, D, 4>(sp, stream);
+    case 8: return stream_t<ES, D, 8>(sp, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int ES, int D, int G>
+static int stream_blocks_per_cu() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_stream<ES, D, G>, 64, 0) !=
+      hipSuccess)
+    return 0;
+  return nb;
+}
+
+int decode_stream_slots(int dtype_bytes, int D, int G) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  int nb = 0;
+#define PKV_SLOTS(ES_, D_)                                 \
+  switch (G) {                                             \
+    case 1: nb = stream_blocks_per_cu<ES_, D_, 1>(); break; \
+    case 2: nb = stream_blocks_per_cu<ES_, D_, 2>(); break; \
+    case 4: nb = stream_blocks_per_cu<ES_, D_, 4>(); break; \
+    case 8: nb = stream_blocks_per_cu<ES_, D_, 8>(); break; \
+  }
+  if (dtype_bytes == 4 && D == 64) { PKV_SLOTS(4, 64) }
+  else if (dtype_bytes == 4 && D == 128) { PKV_SLOTS(4, 128) }
+  else if (dtype_bytes == 2 && D == 64) { PKV_SLOTS(2, 64) }
+  else if (dtype_bytes == 2 && D == 128) { PKV_SLOTS(2, 128) }
+#undef PKV_SLOTS
+  return nb * cus;
+}
+
+static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  StreamParams sp;
+  sp.d = make_decode_params(c, a);
+  sp.total = a.stream_total;
+  sp.waves = a.stream_waves;
+  sp.c0 = a.stream_c0;
+  sp.epoch = a.stream_epoch;
+  sp.counters = a.stream_counters;
+  sp.part_acc = a.stream_acc;
+  sp.part_ml = a.stream_ml;
+  const int G = a.hq / c.hkv;
+  if (c.dtype_bytes == 4) {
+    if (c.head_size == 64) return stream_g<4, 64>(G, sp, stream);
+    if (c.head_size == 128) return stream_g<4, 128>(G, sp, stream);
+  } else {
+    if (c.head_size == 64) return stream_g<2, 64>(G, sp, stream);
+    if (c.head_size == 128) return stream_g<2, 128>(G, sp, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   const DecodeParams p = make_decode_params(c, a);
+  if (a.stream_waves > 0) return launch_decode_stream(c, a, stream);
   const int G = a.hq / c.hkv;
   if (c.dtype_bytes == 4) {
     if (c.head_size == 64) return decode_rows_g<4, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);

@@ -222,3 +222,53 @@ def test_prefill_values_beyond_fp16_range():
         rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
         assert max_abs <= MAX_ABS_BF16 * scale, f"{name}: max|d| {max_abs:.3e} (scale {scale:.3e})"
         assert rel <= REL_L2_BF16, f"{name}: rel L2 {rel:.3e}"
+
+
+def test_one_long_row_split_over_many_waves():
+    """A single 32768-token row: each (row, kv head) item is split over more
+    than 64 waves, so the in-kernel merge walks partials in several chunks."""
+    L = np.array([32768], np.int32)
+    streams = [np.random.default_rng(x) for x in (31, 32, 33, 34)]
+    w = workloads._build(3, "one long row", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                         np.ones(1, np.int32), 2100, streams)
+    _announce("one long row L=32768")
+    st = gpu_step.run_workload(w)
+    _check_attention(st.out.cpu().numpy(), scenario.sequence_attention(w, 0)[None],
+                     "bf16", "one long row")
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_fixed_partition_decode_path(cfg, monkeypatch):
+    """The fixed 256-token split-K path with its separate merge launch
+    (PKV_DECODE_SPLIT=units), which mixed batches also use, on pure decode
+    batches."""
+    monkeypatch.setenv("PKV_DECODE_SPLIT", "units")
+    w = workloads.small(cfg)
+    _announce(f"units split, small config {cfg}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"units split config {cfg}")
+
+
+def test_workspace_reused_with_new_queries():
+    """Two calls in a row on one workspace with different queries: the second
+    call's merged rows must not see partials or counters left by the first."""
+    import copy
+    L = np.array([4000, 33, 2500, 700, 9000, 1], np.int32)
+    streams = [np.random.default_rng(x) for x in (41, 42, 43, 44)]
+    pool = int(1.25 * sum((int(x) + 15) // 16 for x in L)) + 1
+    w = workloads._build(3, "reuse", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                         np.ones(len(L), np.int32), pool, streams)
+    _announce("workspace reuse with new queries")
+    st = gpu_step.run_workload(w)
+    first = st.out.cpu().numpy()
+    w2 = copy.copy(w)
+    rng = np.random.default_rng(45)
+    w2.q = workloads._bf16_codes(rng.standard_normal(w.q.shape).astype(np.float32))
+    st.q.copy_(torch.from_numpy(w2.q.view(np.int16)).cuda())
+    st.attend()
+    torch.cuda.synchronize()
+    second = st.out.cpu().numpy()
+    for s in range(w.batch):
+        _check_attention(first[s:s + 1], scenario.sequence_attention(w, s), "bf16", f"call 1 row {s}")
+        _check_attention(second[s:s + 1], scenario.sequence_attention(w2, s), "bf16", f"call 2 row {s}")

@@ -158,7 +158,16 @@ def test_workspace_sizing():
     lens = np.array([1, 256, 257, 0, 8192], np.int32)
     units = 1 + 1 + 2 + 0 + 32
     header = 256                                      # workspace header
-    assert P.pkv_attention_workspace_bytes(cache, 32, lens) == header + units * 32 * (128 + 2) * 4
+    split_k = header + units * 32 * (128 + 2) * 4
+    # a pure decode batch may instead run the stream kernel: one cost unit per
+    # 32-token step plus one setup unit per (row, kv head); at most one wave
+    # per 8 units, two partials (4 heads x (128 + 2) floats) per wave, then
+    # (256-aligned) one 8-byte counter per (row, kv head)
+    cost = 8 * sum(-(-int(x) // 32) + 1 for x in lens if x > 0)
+    waves = min(4096, -(-cost // 8))
+    ml_end = header + 2 * waves * 4 * 128 * 4 + 2 * waves * 4 * 2 * 4
+    stream = -(-ml_end // 256) * 256 + 5 * 8 * 8
+    assert P.pkv_attention_workspace_bytes(cache, 32, lens) == max(split_k, stream)
     qsl = np.array([0, 1, 2, 3, 3, 1000], np.int32)   # seq 4 is a prefill chunk
     # a prefill sequence of length L adds fp16 V tiles of its blocks, rounded
     # up to whole 64-key tiles, for every kv head, and one int32 exponent each
