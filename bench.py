@@ -3,8 +3,9 @@
 A step is one pass of the whole path over the 8B-shaped GQA decode batch
 (32 query / 8 kv heads, head size 128, bf16, 256 sequences with lognormal
 contexts, median 800, in a 200,000-block pool): block copies (none in this
-workload), the KV write of the 256 new tokens, and decode attention (split-K
-partition pass + merge).  Inputs are resident in HBM before timing starts.
+workload), the KV write of the 256 new tokens, and decode attention (one launch of the
+stream-split kernel, which also merges split rows).  Inputs are resident in
+HBM before timing starts.
 
 Prints one JSON line (rank 0, N = 1).  The roofline object describes the
 attention call, the dominant cost of the step: algorithmic bytes (every
@@ -27,11 +28,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
 # HBM bytes one attention call moves on this workload, from rocprofv3
-# FETCH_SIZE (x2.000, the factor a 1 GiB device copy needs) plus WRITE_SIZE
-# (x1.000) of k_decode_partition and k_decode_merge; see
-# profiles/decode_8b_gqa_b256_traffic.md.  Reset to None whenever either
-# kernel changes until the counters are taken again.
-MEASURED_TRAFFIC_BYTES = 1_389_700_000
+# FETCH_SIZE (scaled by the factor a 1 GiB device copy needs) plus WRITE_SIZE
+# of k_decode_stream; see profiles/decode_8b_gqa_b256_traffic.md.  Reset to
+# None whenever the kernel changes until the counters are taken again.
+MEASURED_TRAFFIC_BYTES = 1_351_737_000
 
 
 def algorithmic_bytes(w) -> int:
@@ -267,7 +267,7 @@ def main() -> None:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": MEASURED_TRAFFIC_BYTES,
-            "kernel": "paged_attention_decode (k_decode_partition + k_decode_merge)",
+            "kernel": "paged_attention_decode (k_decode_stream, one launch)",
             "algorithmic_bytes_per_launch": alg,
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
