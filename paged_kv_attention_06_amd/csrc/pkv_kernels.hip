@@ -857,28 +857,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int hq = hkv * G;
   const int c0 = sp.c0;
 
-  // ---- empty decode rows get zeros: sequences w, w + W, w + 2W, ...
-  for (long long sb = w; sb < p.num_seqs; sb += 64LL * W) {
-    const long long s = sb + (long long)lane * W;
-    bool zero = false;
-    if (s < p.num_seqs) {
-      const int ql = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
-      zero = ql == 1 && p.seq_lens[s] <= 0;
+  // Empty decode rows get zeros: sequences w, w + W, w + 2W, ...  Done at
+  // the end of the wave's work, off the start-up chain of dependent loads.
+  auto zero_rows = [&]() {
+    for (long long sb = w; sb < p.num_seqs; sb += 64LL * W) {
+      const long long s = sb + (long long)lane * W;
+      bool zero = false;
+      if (s < p.num_seqs) {
+        const int ql = p.qsl ? p.qsl[s + 1] - p.qsl[s] : 1;
+        zero = ql == 1 && p.seq_lens[s] <= 0;
+      }
+      unsigned long long m = __ballot(zero);
+      while (m) {
+        const int l = __ffsll(m) - 1;
+        m &= m - 1;
+        const long long sz = sb + (long long)l * W;
+        const int row = p.qsl ? p.qsl[sz] : (int)sz;
+        float* o = p.out + (size_t)row * hq * D;
+        for (int i = lane; i < hq * D; i += 64) o[i] = 0.f;
+      }
     }
-    unsigned long long m = __ballot(zero);
-    while (m) {
-      const int l = __ffsll(m) - 1;
-      m &= m - 1;
-      const long long sz = sb + (long long)l * W;
-      const int row = p.qsl ? p.qsl[sz] : (int)sz;
-      float* o = p.out + (size_t)row * hq * D;
-      for (int i = lane; i < hq * D; i += 64) o[i] = 0.f;
-    }
-  }
+  };
 
   const long long cs = (long long)w * T / W;
   const long long ce = (long long)(w + 1) * T / W;
-  if (cs >= ce) return;
+  if (cs >= ce) {
+    zero_rows();
+    return;
+  }
 
   // ---- find the sequence whose cost range holds cs; keep its chunk of 256
   // decode lengths (and output rows) in LDS for the walk
@@ -936,7 +942,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
     base += total;
   }
-  if (s_found < 0) return;
+  if (s_found < 0) {
+    zero_rows();
+    return;
+  }
   load_chunk(s0);
 
   auto len_of = [&](int s) -> int {  // decode length of sequence s (chunk reloaded on demand)
@@ -963,7 +972,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     cur0.j = (int)max(0LL, cs - cur0.A);
     cur0.valid = cur0.A + cur0.j < ce;
   }
-  if (!cur0.valid) return;
+  if (!cur0.valid) {
+    zero_rows();
+    return;
+  }
 
   auto next = [&](const StreamCur& c) {
     StreamCur r = c;
@@ -1226,6 +1238,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     cur1 = c3;
   }
 
+  zero_rows();
   // ---- count this wave into its split items (lanes 0 and 1 at once, after
   // its partial stores are complete); the last contributor merges.
   if (npend == 0) return;
