@@ -272,3 +272,19 @@ def test_workspace_reused_with_new_queries():
     for s in range(w.batch):
         _check_attention(first[s:s + 1], scenario.sequence_attention(w, s), "bf16", f"call 1 row {s}")
         _check_attention(second[s:s + 1], scenario.sequence_attention(w2, s), "bf16", f"call 2 row {s}")
+
+
+def test_prefill_chunk_rows_dense_sample():
+    """The 1950-row prefill chunk on 1048 cached tokens: its q tiles need 17
+    to 47 key tiles and are split into key chunks merged in-launch, so every
+    7th row (and the last) is checked against the oracle."""
+    w = workloads.make(4)
+    _announce(f"prefill chunk dense sample: T={w.num_tokens}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    s = int(np.argmax(w.q_len))
+    ql = int(w.q_len[s])
+    rows = sorted(set(range(0, ql, 7)) | {ql - 1})
+    ref = scenario.sequence_attention(w, s, rows)
+    got = out[int(w.query_start_loc[s]) + np.asarray(rows)]
+    _check_attention(got, ref, "bf16", "prefill chunk rows")
