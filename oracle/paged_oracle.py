@@ -52,8 +52,8 @@ BLOCK_SIZE = 16
 # ----------------------------------------------------------------------------
 # element types: codes are the raw stored bit patterns
 # ----------------------------------------------------------------------------
-_CODE = {"f32": np.uint32, "bf16": np.uint16}
-_BYTES = {"f32": 4, "bf16": 2}
+_CODE = {"f32": np.uint32, "bf16": np.uint16, "fp8": np.uint8}
+_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 def code_dtype(dtype: str):
@@ -71,7 +71,65 @@ def decode(codes: np.ndarray, dtype: str) -> np.ndarray:
         return (codes.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     if dtype == "f32":
         return np.ascontiguousarray(codes).view(np.float32).astype(np.float64)
+    if dtype == "fp8":
+        return e4m3_table()[np.asarray(codes, dtype=np.uint8)]
     raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# FP8 KV cache (the pages list an FP8 KV cache that halves its memory at
+# nearly no accuracy cost: vLLM 技术内幕 section 7.2; Continuous batching +
+# PagedAttention Q&A).  Reading taken here: codes are OCP FP8 E4M3 (1 sign
+# bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, exponent
+# and mantissa all ones = NaN, largest finite 448); each cache has one K scale
+# and one V scale; a stored code c stands for e4m3(c) * scale; a written value
+# x becomes the code nearest to x * (1 / scale) (both products in float32,
+# ties to the even code), saturated to +-448.
+# ----------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """The number an E4M3 code stands for (NaN for 0x7F and 0xFF)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:                              # subnormal: man * 2^-3 * 2^(1-7)
+        return sign * man * 2.0 ** -9
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+def e4m3_table() -> np.ndarray:
+    """float64 value of every code 0..255."""
+    return np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """float values -> E4M3 codes: the nearest representable magnitude, ties
+    to the even code, magnitudes above 448 saturated to 448, NaN to 0x7F
+    (with its sign bit); the sign of zero is kept."""
+    y = np.asarray(y, dtype=np.float64)
+    mags = e4m3_table()[:0x7F]                # codes 0x00..0x7E, increasing
+    a = np.minimum(np.abs(y), E4M3_MAX)
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)  # first >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - mags[lo]
+    d_hi = mags[hi] - a
+    pick = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    pick = np.where(mags[hi] == a, hi, pick)
+    sign = np.signbit(y).astype(np.uint8) << np.uint8(7)
+    codes = (pick.astype(np.uint8) | sign)
+    return np.where(np.isnan(y), np.uint8(0x7F) | sign, codes).astype(np.uint8)
+
+
+def fp8_quantize(codes_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """bf16 codes -> E4M3 codes of x * (1 / scale), both steps in float32."""
+    inv = np.float32(1.0) / np.float32(scale)
+    x = (np.asarray(codes_bf16, dtype=np.uint32) << np.uint32(16)).view(np.float32)
+    return e4m3_encode((x * inv).astype(np.float32))
 
 
 # ----------------------------------------------------------------------------
@@ -205,10 +263,15 @@ class CowPool:
 # the two data movements
 # ----------------------------------------------------------------------------
 def kv_write(pool: np.ndarray, dtype: str, k_new: np.ndarray, v_new: np.ndarray,
-             slots, block_size: int = BLOCK_SIZE) -> None:
+             slots, block_size: int = BLOCK_SIZE, k_scale: float = 1.0,
+             v_scale: float = 1.0) -> None:
     """Scatter each new token's K and V rows (all kv heads) to its slot, in
     place (vLLM 技术内幕 2.1: write_to_paged_cache / reshape_and_cache).
-    k_new, v_new: codes [T][Hkv][D].  A negative slot is skipped."""
+    k_new, v_new: codes [T][Hkv][D] of the cache's type, or bf16 codes for an
+    FP8 cache, which stores them quantized.  A negative slot is skipped."""
+    if dtype == "fp8":
+        k_new = fp8_quantize(k_new, k_scale)
+        v_new = fp8_quantize(v_new, v_scale)
     D = k_new.shape[2]
     kidx = k_tile_index(D, dtype, block_size)
     vidx = v_tile_index(D, dtype, block_size)
@@ -272,17 +335,20 @@ def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, positions, scale
 
 def paged_attention(pool: np.ndarray, dtype: str, q_codes: np.ndarray, block_tables,
                     seq_lens, query_start_loc, scale: float,
-                    block_size: int = BLOCK_SIZE) -> np.ndarray:
+                    block_size: int = BLOCK_SIZE, k_scale: float = 1.0,
+                    v_scale: float = 1.0) -> np.ndarray:
     """Attention of a flattened batch of query rows over the paged cache.
 
-    q_codes: codes [T][Hq][D]; sequence s owns rows
+    q_codes: codes [T][Hq][D] (bf16 for an FP8 cache, whose stored codes
+    stand for e4m3 value * k_scale or * v_scale); sequence s owns rows
     query_start_loc[s] .. query_start_loc[s+1]-1 (Inside vLLM "Forward pass":
     one super-sequence, each sequence attending only to its own tokens).
     A sequence of length 0 yields zeros.  Returns float64 [T][Hq][D].
     """
     T, Hq, D = q_codes.shape
     out = np.zeros((T, Hq, D), dtype=np.float64)
-    q = decode(q_codes, dtype)
+    q = decode(q_codes, "bf16" if dtype == "fp8" else dtype)
+    ks, vs = (float(k_scale), float(v_scale)) if dtype == "fp8" else (1.0, 1.0)
     for s in range(len(seq_lens)):
         L = int(seq_lens[s])
         r0, r1 = int(query_start_loc[s]), int(query_start_loc[s + 1])
@@ -290,5 +356,6 @@ def paged_attention(pool: np.ndarray, dtype: str, q_codes: np.ndarray, block_tab
             continue
         K, V = gather_kv(pool, dtype, block_tables[s], L, D, block_size)
         positions = [L - (r1 - r0) + i for i in range(r1 - r0)]
-        out[r0:r1] = attention_rows(q[r0:r1], decode(K, dtype), decode(V, dtype), positions, scale)
+        out[r0:r1] = attention_rows(q[r0:r1], decode(K, dtype) * ks, decode(V, dtype) * vs,
+                                    positions, scale)
     return out

@@ -23,7 +23,9 @@ def build_tables(w, with_pool: bool = True):
     """Steps 1-3.  Returns a dict with the pool (or None), block tables
     (lists), the step's slots and COW pairs, and the allocator."""
     alloc = po.CowPool(w.num_blocks, w.free_order)
-    pool = po.new_pool(w.num_blocks, w.num_kv_heads, w.head_size, w.dtype, w.pool_fill) \
+    kvd = w.kv_dtype
+    wr = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+    pool = po.new_pool(w.num_blocks, w.num_kv_heads, w.head_size, kvd, w.pool_fill) \
         if with_pool else None
 
     prompt_tables = []
@@ -32,7 +34,7 @@ def build_tables(w, with_pool: bool = True):
         slots, _ = alloc.append(table, 0, int(w.prompt_len[p]))
         if with_pool:
             a, b = int(w.prompt_start[p]), int(w.prompt_start[p + 1])
-            po.kv_write(pool, w.dtype, w.prompt_k[a:b], w.prompt_v[a:b], slots)
+            po.kv_write(pool, kvd, w.prompt_k[a:b], w.prompt_v[a:b], slots, **wr)
         prompt_tables.append(table)
 
     tables = [None] * w.batch
@@ -43,7 +45,7 @@ def build_tables(w, with_pool: bool = True):
         slots, _ = alloc.append(table, 0, int(w.hist_len[s]))
         if with_pool:
             a, b = int(w.hist_start[s]), int(w.hist_start[s + 1])
-            po.kv_write(pool, w.dtype, w.hist_k[a:b], w.hist_v[a:b], slots)
+            po.kv_write(pool, kvd, w.hist_k[a:b], w.hist_v[a:b], slots, **wr)
         tables[s] = table
     for s in range(w.batch):
         if w.fork_of[s] >= 0:
@@ -77,11 +79,13 @@ def run_step(w):
     final pool and the float64 attention output [T][Hq][D]."""
     st = build_tables(w, with_pool=True)
     po.block_copy(st["pool"], st["cow_pairs"])
-    po.kv_write(st["pool"], w.dtype, w.new_k, w.new_v, st["slots"])
+    po.kv_write(st["pool"], w.kv_dtype, w.new_k, w.new_v, st["slots"], k_scale=w.k_scale,
+                v_scale=w.v_scale)
     bt = table_matrix(st["tables"])
     st["block_tables"] = bt
-    st["out"] = po.paged_attention(st["pool"], w.dtype, w.q, bt, w.seq_lens,
-                                   w.query_start_loc, w.scale)
+    st["out"] = po.paged_attention(st["pool"], w.kv_dtype, w.q, bt, w.seq_lens,
+                                   w.query_start_loc, w.scale, k_scale=w.k_scale,
+                                   v_scale=w.v_scale)
     return st
 
 
@@ -114,4 +118,8 @@ def sequence_attention(w, s: int, rows=None) -> np.ndarray:
     rows = list(rows)
     q = po.decode(w.q[qsl[s] + np.asarray(rows, np.int64)], w.dtype)
     positions = [L - q_len + i for i in rows]
+    if w.kv_dtype == "fp8":       # what an FP8 cache holds: the quantized values
+        Kf = po.decode(po.fp8_quantize(K, w.k_scale), "fp8") * w.k_scale
+        Vf = po.decode(po.fp8_quantize(V, w.v_scale), "fp8") * w.v_scale
+        return po.attention_rows(q, Kf, Vf, positions, w.scale)
     return po.attention_rows(q, po.decode(K, w.dtype), po.decode(V, w.dtype), positions, w.scale)

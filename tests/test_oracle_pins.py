@@ -326,3 +326,117 @@ def test_config5_forks_all_copy_on_write():
     shared_last = st["prompt_tables"][0][-1]
     assert all(int(p[0]) == shared_last for p in st["cow_pairs"])
     assert st["alloc"].ref[shared_last] == 1        # only the owner holds it now
+
+
+# ------------------------------------------------------------- FP8 KV cache
+def _torch_e4m3(codes: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_decode_matches_torch_for_every_code():
+    """The library routine: torch's float8_e4m3fn reads all 256 codes the
+    same way (NaN at 0x7F and 0xFF only)."""
+    mine = po.e4m3_table()
+    ref = _torch_e4m3(np.arange(256))
+    assert np.array_equal(np.isnan(mine), np.isnan(ref))
+    assert np.isnan(mine).sum() == 2 and np.isnan(mine[0x7F]) and np.isnan(mine[0xFF])
+    ok = ~np.isnan(ref)
+    assert np.array_equal(mine[ok], ref[ok])
+    assert np.array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+
+
+def test_e4m3_format_values():
+    """Values the E4M3 definition fixes: bias 7, 3 mantissa bits, subnormals
+    at exponent field 0, largest finite 448."""
+    assert po.e4m3_value(0x38) == 1.0            # exponent field 7, mantissa 0
+    assert po.e4m3_value(0x7E) == 448.0          # 1.75 * 2^8
+    assert po.e4m3_value(0x08) == 2.0 ** -6      # smallest normal
+    assert po.e4m3_value(0x01) == 2.0 ** -9      # smallest subnormal
+    assert po.e4m3_value(0x07) == 7 * 2.0 ** -9  # largest subnormal
+    assert po.e4m3_value(0xC0) == -2.0
+    assert po.e4m3_value(0x80) == 0.0 and math.copysign(1, po.e4m3_value(0x80)) < 0
+    values = po.e4m3_table()[:0x7F]
+    assert np.all(np.diff(values) > 0)           # codes 0..126 increase strictly
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    """Within |x| <= 464 (where no saturation applies) the encoder rounds to
+    nearest with ties to the even code, as torch's cast does; the tests use
+    random values, every representable value, and every midpoint (a tie)."""
+    rng = np.random.default_rng(3)
+    vals = po.e4m3_table()[:0x7F]
+    mids = (vals[1:] + vals[:-1]) / 2
+    x = np.concatenate([rng.standard_normal(20000) * 50, rng.uniform(-464, 464, 20000),
+                        rng.uniform(-0.02, 0.02, 20000), vals, -vals, mids, -mids,
+                        [464.0, -464.0, 0.0, 2.0 ** -10, 2.0 ** -11]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(po.e4m3_encode(x), ref)
+
+
+def test_e4m3_encode_saturates_and_keeps_nan():
+    big = np.array([465.0, 480.0, 1e6, 3.0e38, np.inf], np.float32)
+    assert np.all(po.e4m3_encode(big) == 0x7E)
+    assert np.all(po.e4m3_encode(-big) == 0xFE)
+    assert po.e4m3_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert np.array_equal(po.e4m3_encode(po.e4m3_table()[codes]), codes)  # round trip
+
+
+def test_fp8_quantize_is_float32_product_then_cast():
+    """x * (1 / scale), both in float32, then the cast: checked against torch
+    doing the same float32 arithmetic, for bf16 inputs in range."""
+    rng = np.random.default_rng(4)
+    codes = workloads._bf16_codes(rng.standard_normal(50000).astype(np.float32) * 2)
+    for scale in (workloads.FP8_SCALE, 0.37, 3.0):
+        x = torch.from_numpy(codes.astype(np.int16)).view(torch.bfloat16).float()
+        y = x * (torch.tensor(1.0, dtype=torch.float32) / torch.tensor(scale, dtype=torch.float32))
+        y = torch.clamp(y, -448, 448)
+        ref = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(po.fp8_quantize(codes, scale), ref)
+
+
+def test_fp8_pool_bytes_halve():
+    """Per-block byte formula with one byte per element."""
+    assert po.block_bytes(16, 8, 128, po.dtype_bytes("fp8")) == 32768
+    assert po.new_pool(3, 8, 128, "fp8", 0x7F).nbytes == 3 * 32768
+
+
+def test_fp8_paged_equals_contiguous_on_dequantized_values():
+    """The FP8 step's output equals textbook attention (separately written
+    einsum) on the quantized K/V times their scales."""
+    w = workloads.make_fp8(3, small_size=True)
+    st = scenario.run_step(w)
+    qsl = w.query_start_loc
+    G = w.num_q_heads // w.num_kv_heads
+    table = _torch_e4m3(np.arange(256))
+    for s in range(w.batch):
+        K, V = scenario.sequence_kv(w, s)
+        Kq = torch.from_numpy(K.astype(np.int16)).view(torch.bfloat16).float() * (1 / np.float32(w.k_scale))
+        Vq = torch.from_numpy(V.astype(np.int16)).view(torch.bfloat16).float() * (1 / np.float32(w.v_scale))
+        Kd = table[Kq.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()] * w.k_scale
+        Vd = table[Vq.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()] * w.v_scale
+        L, q_len = int(w.seq_lens[s]), int(w.q_len[s])
+        q = po.decode(w.q[qsl[s]:qsl[s + 1]], "bf16")
+        ref = _dense_attention_einsum(q, Kd, Vd, [L - q_len + i for i in range(q_len)], w.scale, G)
+        np.testing.assert_allclose(st["out"][qsl[s]:qsl[s + 1]], ref, rtol=0, atol=1e-13)
+
+
+def test_fp8_kv_write_layout_and_skip():
+    """An FP8 write stores each quantized element at the layout's byte and
+    leaves every other byte (and skipped tokens) untouched."""
+    rng = np.random.default_rng(5)
+    pool = po.new_pool(6, 2, 64, "fp8", 0x7F)
+    k = workloads._bf16_codes(rng.standard_normal((3, 2, 64)).astype(np.float32))
+    v = workloads._bf16_codes(rng.standard_normal((3, 2, 64)).astype(np.float32))
+    slots = [5 * 16 + 3, -1, 2 * 16 + 15]
+    po.kv_write(pool, "fp8", k, v, slots, k_scale=0.25, v_scale=0.5)
+    kq, vq = po.fp8_quantize(k, 0.25), po.fp8_quantize(v, 0.5)
+    for t, slot in ((0, slots[0]), (2, slots[2])):
+        blk, off = divmod(slot, 16)
+        for hh in range(2):
+            for d in range(64):
+                # K granule: 16 consecutive d of one token; V granule: 16 tokens of one d
+                assert pool[blk, hh, 0, ((d // 16) * 16 + off) * 16 + d % 16] == kq[t, hh, d]
+                assert pool[blk, hh, 1, d * 16 + off] == vq[t, hh, d]
+    touched = 2 * 2 * 2 * 64
+    assert int((pool != 0x7F).sum()) <= touched

@@ -37,6 +37,10 @@ import numpy as np
 BLOCK_SIZE = 16
 BF16_NAN = 0x7FC0
 F32_NAN = 0x7FC00000
+FP8_NAN = 0x7F
+# FP8 KV caches of the FP8 variants: one K and one V scale per cache.  Values
+# are N(0,1); with scale 1/64 the largest E4M3 magnitude 448 stands for 7.
+FP8_SCALE = 1.0 / 64.0
 
 
 @dataclass
@@ -67,6 +71,17 @@ class Workload:
     q: np.ndarray               # [T][Hq][D]
     pool_fill: int              # code every pool element holds before use (NaN)
     extra: dict = field(default_factory=dict)
+    cache_dtype: str = ""       # "" = dtype; "fp8" = E4M3 cache written from bf16 values
+    k_scale: float = 1.0        # FP8 cache: a stored code stands for e4m3 value * scale
+    v_scale: float = 1.0
+
+    @property
+    def kv_dtype(self) -> str:
+        return self.cache_dtype or self.dtype
+
+    @property
+    def kv_dtype_bytes(self) -> int:
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
 
     @property
     def batch(self) -> int:
@@ -117,7 +132,8 @@ def _pool_size(lengths, factor: float, extra_blocks: int = 0) -> int:
 
 def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, scale: float,
            hist_len, q_len, num_blocks: int, streams, fork_of=None, prompt_len=(),
-           owner_ref=False, extra=None, values: bool = True) -> Workload:
+           owner_ref=False, extra=None, values: bool = True, cache_dtype: str = "",
+           kv_scale: float = 1.0) -> Workload:
     _, r_blocks, r_vals, _ = streams
     hist_len = np.asarray(hist_len, dtype=np.int32)
     q_len = np.asarray(q_len, dtype=np.int32)
@@ -145,9 +161,23 @@ def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, sca
         new_k=_values(r_vals, (T, Hkv, D), dtype, values),
         new_v=_values(r_vals, (T, Hkv, D), dtype, values),
         q=_values(r_vals, (T, Hq, D), dtype, values),
-        pool_fill=F32_NAN if dtype == "f32" else BF16_NAN,
+        pool_fill=FP8_NAN if cache_dtype == "fp8" else (F32_NAN if dtype == "f32" else BF16_NAN),
         extra=extra or {},
+        cache_dtype=cache_dtype, k_scale=kv_scale, v_scale=kv_scale,
     )
+    return w
+
+
+def make_fp8(config_id: int, seed: int = 0, small_size: bool = False) -> Workload:
+    """A bf16 workload (configs 2, 3 or 5, full or small) whose KV cache is
+    FP8 E4M3 with K and V scales of 1/64: same lengths, blocks and drawn
+    values; the cache stores them quantized."""
+    w = small(config_id, seed) if small_size else make(config_id, seed)
+    assert w.dtype == "bf16"
+    w.name = w.name + " (fp8 KV)"
+    w.cache_dtype = "fp8"
+    w.k_scale = w.v_scale = FP8_SCALE
+    w.pool_fill = FP8_NAN
     return w
 
 
