@@ -57,7 +57,13 @@ enum {
   PKV_ERR_RANGE = 7      /* a host-visible index or length is out of range  */
 };
 
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+/* Element types of a cache.  PKV_FP8_E4M3 stores OCP FP8 E4M3 codes (1 sign
+ * bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7F and
+ * 0xFF are NaN, largest finite 448) with one scale for K and one for V: a
+ * stored code c stands for e4m3(c) * k_scale (or v_scale).  The pages list an
+ * FP8 KV cache that halves its memory (vLLM 技术内幕, section 7.2); codes and
+ * scales are this library's reading. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 };
 
 /* Static text for a status code. */
 const char* pkv_status_string(int status);
@@ -73,7 +79,9 @@ typedef struct pkv_cache {
   int32_t block_size;   /* tokens per block; must be 16                      */
   int32_t num_kv_heads; /* >= 1                                              */
   int32_t head_size;    /* 64 or 128                                         */
-  int32_t dtype;        /* PKV_F32 or PKV_BF16                               */
+  int32_t dtype;        /* PKV_F32, PKV_BF16 or PKV_FP8_E4M3                 */
+  float k_scale;        /* PKV_FP8_E4M3: finite, > 0; ignored otherwise      */
+  float v_scale;        /* PKV_FP8_E4M3: finite, > 0; ignored otherwise      */
 } pkv_cache;
 
 /* Bytes of one block over all kv heads, K and V:
@@ -104,7 +112,11 @@ int pkv_build_slot_mapping(const int32_t* block_tables, int32_t max_blocks_per_s
 /* Write each new token's K and V rows, all kv heads, into its slot
  * (vLLM 技术内幕 section 2.1: write_to_paged_cache / reshape_and_cache).
  *   k_new, v_new  device [num_tokens][num_kv_heads][head_size], contiguous,
- *                 same element type as the cache (bits are copied as is)
+ *                 same element type as the cache (bits are copied as is);
+ *                 for a PKV_FP8_E4M3 cache they are bf16 and each value x is
+ *                 stored as the E4M3 code nearest to x * (1 / scale) (both
+ *                 float32 operations; ties to the even code; magnitudes
+ *                 above 448 saturate to 448; NaN stays NaN)
  *   slot_mapping  device int64 [num_tokens]; slot < 0 skips the token.
  * Preconditions on device data: non-negative slots are distinct and
  * < num_blocks * 16.  num_tokens == 0 is a no-op. */
@@ -141,6 +153,8 @@ size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads
  * h / (num_q_heads / num_kv_heads).
  *   out           device float32 [num_seqs][num_q_heads][head_size]
  *   q             device [num_seqs][num_q_heads][head_size], cache dtype
+ *                 (bf16 for a PKV_FP8_E4M3 cache, whose K and V are read as
+ *                 their codes' values times k_scale and v_scale)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs]
  *   h_seq_lens    host copy of seq_lens (sizes the grid; must be equal)
@@ -162,7 +176,8 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
  * and sees keys 0..that position (causal).  The step's own K/V must already
  * be written (paged_kv_write on the same stream).
  *   out    device float32 [num_tokens][num_q_heads][head_size]
- *   q      device [num_tokens][num_q_heads][head_size], cache dtype
+ *   q      device [num_tokens][num_q_heads][head_size], cache dtype (bf16 for
+ *          a PKV_FP8_E4M3 cache; rows with q_len > 1 need a bf16 cache)
  *   query_start_loc, seq_lens: device int32; h_*: equal host copies
  *   num_tokens == query_start_loc[num_seqs]
  * Host-checked: q_len_s <= seq_lens[s] <= max_blocks_per_seq * 16. */

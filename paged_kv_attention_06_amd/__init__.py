@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     PKV_BF16,
     PKV_F32,
+    PKV_FP8_E4M3,
     Cache,
     PkvCache,
     PkvError,

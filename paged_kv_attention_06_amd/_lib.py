@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 STATUS = {0: "PKV_OK", 1: "PKV_ERR_NULL", 2: "PKV_ERR_DIM", 3: "PKV_ERR_DTYPE",
           4: "PKV_ERR_WORKSPACE", 5: "PKV_ERR_HIP", 6: "PKV_ERR_NOMEM", 7: "PKV_ERR_RANGE"}
 
@@ -32,7 +33,8 @@ _vp = ctypes.c_void_p
 class PkvCache(ctypes.Structure):
     _fields_ = [("kv", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
                 ("block_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 def _sig(name, res, args):
@@ -134,18 +136,20 @@ class Cache:
     """Descriptor of a KV pool living in a torch tensor of raw bytes."""
 
     def __init__(self, kv, num_blocks: int, num_kv_heads: int, head_size: int, dtype: int,
-                 block_size: int = 16):
+                 block_size: int = 16, k_scale: float = 1.0, v_scale: float = 1.0):
         self.kv = kv
         self.desc = PkvCache(kv.data_ptr() if kv is not None else 0, num_blocks, block_size,
-                             num_kv_heads, head_size, dtype)
+                             num_kv_heads, head_size, dtype, k_scale, v_scale)
 
     @property
     def ref(self):
         return ctypes.byref(self.desc)
 
 
-def descriptor(num_blocks, num_kv_heads, head_size, dtype, block_size=16, kv_ptr=0) -> PkvCache:
-    return PkvCache(kv_ptr, num_blocks, block_size, num_kv_heads, head_size, dtype)
+def descriptor(num_blocks, num_kv_heads, head_size, dtype, block_size=16, kv_ptr=0,
+               k_scale=1.0, v_scale=1.0) -> PkvCache:
+    return PkvCache(kv_ptr, num_blocks, block_size, num_kv_heads, head_size, dtype, k_scale,
+                    v_scale)
 
 
 def pkv_block_bytes(desc: PkvCache) -> int:

@@ -3,6 +3,7 @@
 #include <atomic>
 #include <chrono>
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdlib>
 #include <cstdio>
@@ -38,6 +39,7 @@ int dtype_bytes(int32_t dtype) {
   switch (dtype) {
     case PKV_F32: return 4;
     case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
   }
   return 0;
 }
@@ -55,6 +57,17 @@ int check_cache(const pkv_cache* c, pkv::CacheDesc* d, bool need_kv = true) {
     return fail(PKV_ERR_DIM, "head_size %d unsupported (64 or 128)", c->head_size);
   const int es = dtype_bytes(c->dtype);
   if (!es) return fail(PKV_ERR_DTYPE, "dtype %d unsupported", c->dtype);
+  d->fp8 = c->dtype == PKV_FP8_E4M3;
+  d->k_scale = d->v_scale = d->k_inv = d->v_inv = 1.f;
+  if (d->fp8) {
+    if (!(c->k_scale > 0.f && c->k_scale < INFINITY && c->v_scale > 0.f && c->v_scale < INFINITY))
+      return fail(PKV_ERR_RANGE, "fp8 cache scales must be finite and > 0 (k %g, v %g)",
+                  (double)c->k_scale, (double)c->v_scale);
+    d->k_scale = c->k_scale;
+    d->v_scale = c->v_scale;
+    d->k_inv = 1.f / c->k_scale;
+    d->v_inv = 1.f / c->v_scale;
+  }
   d->kv = static_cast<char*>(c->kv);
   d->num_blocks = c->num_blocks;
   d->hkv = c->num_kv_heads;
@@ -192,6 +205,8 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   if (int e = plan_attention(mixed ? h_qsl : nullptr, h_seq_lens, num_seqs, max_blocks,
                              num_q_heads / c.hkv, &plan))
     return e;
+  if (plan.prefill_tiles > 0 && c.fp8)
+    return fail(PKV_ERR_DTYPE, "rows with q_len > 1 need a bf16 cache (this one is fp8)");
   if (plan.prefill_tiles > 0 && !pkv::prefill_supported(num_q_heads / c.hkv, c.dtype_bytes))
     return fail(PKV_ERR_DTYPE,
                 "rows with q_len > 1 need a bf16 cache and 1, 2 or 4 query heads per kv head");
@@ -215,7 +230,8 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.seq_lens = seq_lens;
   a.query_start_loc = mixed ? qsl : nullptr;
   a.num_seqs = num_seqs;
-  a.scale = scale;
+  a.scale = scale * c.k_scale;  // an fp8 cache's K scale folds into the score scale
+  a.out_scale = c.v_scale;      // and its V scale into the output
   char* ws = static_cast<char*>(workspace);
   a.ws_acc = ws ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;
   a.ws_ml = a.ws_acc ? a.ws_acc + (size_t)plan.decode_units * num_q_heads * c.head_size : nullptr;
@@ -229,7 +245,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   a.stream_waves = 0;
-  if (plan.prefill_tiles == 0 && plan.decode_units > 0 && stream_decode_enabled()) {
+  if (plan.prefill_tiles == 0 && plan.decode_units > 0 && (stream_decode_enabled() || c.fp8)) {
     const int G = num_q_heads / c.hkv;
     const int slots = pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
     int64_t waves = stream_wave_cap(plan, c.hkv);
@@ -249,6 +265,8 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
       a.stream_counters = reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off);
     }
   }
+  if (c.fp8 && plan.decode_units > 0 && a.stream_waves == 0)
+    return fail(PKV_ERR_HIP, "fp8 decode needs the device's wave count (hipGetDevice failed)");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.prefill_tiles > 0 && plan.decode_units > 0)
     return hip_status(pkv::launch_mixed_rows(c, a, st), "mixed rows");

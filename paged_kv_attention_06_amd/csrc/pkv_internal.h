@@ -35,6 +35,9 @@ struct CacheDesc {
   int head_size;
   int dtype_bytes;
   size_t block_bytes;  // 2 * 16 * hkv * D * es
+  bool fp8;            // E4M3 codes; new rows and queries are bf16
+  float k_scale, v_scale;  // fp8: a code stands for e4m3 value * scale
+  float k_inv, v_inv;      // fp8: 1 / scale in float32, the write's multiplier
 };
 
 struct AttnDesc {
@@ -47,6 +50,7 @@ struct AttnDesc {
   const int32_t* query_start_loc;  // nullptr: pure decode, row s = sequence s
   int num_seqs;
   float scale;
+  float out_scale;                 // multiplies the output (the V scale of an fp8 cache)
   float* ws_acc;                   // [units][hq][D]
   float* ws_ml;                    // [units][hq][2]
   int64_t decode_units;            // split-K work units over all decode rows

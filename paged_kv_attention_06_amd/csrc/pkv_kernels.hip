@@ -43,6 +43,33 @@ __device__ __forceinline__ float granule_elem(const uint4& g, int e) {
   }
 }
 
+// ---- FP8 E4M3 (OCP): encode with round to nearest even, saturating
+// magnitudes above 448 to 448; `sign` supplies the sign bit (0 or 0x80).
+__device__ __forceinline__ uint32_t e4m3_code(float y, uint32_t sign) {
+  const uint32_t au = __float_as_uint(y) & 0x7FFFFFFFu;
+  if (au > 0x7F800000u) return sign | 0x7Fu;           // NaN
+  const float a = __uint_as_float(au);
+  if (a >= 448.f) return sign | 0x7Eu;                 // saturate (infinities too)
+  if (a < 0.015625f)                                   // below 2^-6: steps of 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.f);  // 0..8 (8 = smallest normal)
+  const uint32_t e = (au >> 23) - 120u;                // E4M3 biased exponent, 1..15
+  uint32_t m = (au >> 20) & 7u;
+  const uint32_t rest = au & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;  // a carry bumps e
+  return sign | ((e << 3) + m);
+}
+
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+// Two E4M3 codes (bytes 2 HI, 2 HI + 1 of w) -> two floats / two bf16.
+template <bool HI>
+__device__ __forceinline__ f32x2v_t fp8x2_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -125,8 +152,65 @@ __global__ __launch_bounds__(256) void k_kv_write(char* __restrict__ kv, size_t 
   }
 }
 
+// FP8 cache: one thread per (token, kv head, 16 consecutive d).  It reads the
+// 16 bf16 inputs of K and of V, quantizes them (x * (1 / scale) in float32,
+// then the nearest E4M3 code) and writes one 16-byte K granule and 16 bytes
+// of the V tile (one per d, at the token's offset in that d's granule).
+__global__ __launch_bounds__(256) void k_kv_write_fp8(char* __restrict__ kv, size_t block_bytes,
+                                                      int hkv, int D,
+                                                      const uint4* __restrict__ k_new,
+                                                      const uint4* __restrict__ v_new,
+                                                      const int64_t* __restrict__ slots,
+                                                      int64_t total, float k_inv, float v_inv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int KG = D / 16;
+  const int c = (int)(i % KG);
+  const int64_t r = i / KG;            // row (token, kv head)
+  const int h = (int)(r % hkv);
+  const int64_t t = r / hkv;
+  const int64_t slot = slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
+  char* head = kv + blk * (int64_t)block_bytes + (int64_t)h * (2 * BS * D);
+  auto quantize16 = [](const uint4* src, float inv, uint32_t (&out)[4]) {
+    const uint4 a = src[0], b = src[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bits = (w[(4 * q + e) >> 1] >> (((4 * q + e) & 1) * 16)) & 0xFFFFu;
+        const float x = __uint_as_float(bits << 16);
+        word |= e4m3_code(x * inv, (bits >> 8) & 0x80u) << (8 * e);
+      }
+      out[q] = word;
+    }
+  };
+  const int64_t src = r * (D / 8) + 2 * c;  // 16 bf16 = two uint4
+  uint32_t kq[4], vq[4];
+  quantize16(k_new + src, k_inv, kq);
+  quantize16(v_new + src, v_inv, vq);
+  // K: granule c of token `off` sits at (c * BS + off) * 16
+  *reinterpret_cast<uint4*>(head + (c * BS + off) * 16) = make_uint4(kq[0], kq[1], kq[2], kq[3]);
+  // V: element (off, d) at d * 16 + off (one 16-token granule per d)
+  unsigned char* vt = reinterpret_cast<unsigned char*>(head + BS * D);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) vt[(c * 16 + e) * 16 + off] = (unsigned char)(vq[e >> 2] >> (8 * (e & 3)));
+}
+
 hipError_t launch_kv_write(const CacheDesc& c, const void* k_new, const void* v_new,
                            const int64_t* slots, int64_t num_tokens, hipStream_t stream) {
+  if (c.fp8) {
+    const int64_t total = num_tokens * c.hkv * (c.head_size / 16);
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_kv_write_fp8, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                       c.kv, c.block_bytes, c.hkv, c.head_size, (const uint4*)k_new,
+                       (const uint4*)v_new, slots, total, c.k_inv, c.v_inv);
+    return hipGetLastError();
+  }
   const int64_t total = num_tokens * c.hkv * (c.head_size * c.dtype_bytes / 16);
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 255) / 256));
@@ -283,6 +367,7 @@ struct DecodeParams {
   const int32_t* qsl;
   int num_seqs;
   float scale_log2;
+  float out_scale;  // multiplies every output (an fp8 cache's V scale)
   float* ws_acc;
   float* ws_ml;
   int full_units;   // units [0, full_units) are full partitions
@@ -322,6 +407,34 @@ __device__ __forceinline__ void pv_block(const uint4 (&vr)[BS * D * ES / 16 / 64
   }
 }
 
+// P.V over one block of an fp8 cache: vr[dd] holds the 16 keys' E4M3 codes
+// of d = 64 dd + lane (one granule per d), converted two at a time.
+template <int D, int G, bool CHECK>
+__device__ __forceinline__ void pv_block_fp8(const uint4 (&vr)[D / 64], const float* __restrict__ p_lds,
+                                             int key_base, int valid_keys, float (&acc)[G][D / 64]) {
+  constexpr int DPL = D / 64;
+  float pk[16][G];
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+#pragma unroll
+    for (int g = 0; g < G; ++g) pk[e][g] = p_lds[(key_base + e) * G + g];
+#pragma unroll
+  for (int dd = 0; dd < DPL; ++dd) {
+    const uint32_t w[4] = {vr[dd].x, vr[dd].y, vr[dd].z, vr[dd].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x2v_t v = (q & 1) ? fp8x2_f32<true>(w[q >> 1]) : fp8x2_f32<false>(w[q >> 1]);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int e = 2 * q + k;
+        if (CHECK && e >= valid_keys) continue;
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(pk[e][g], v[k], acc[g][dd]);
+      }
+    }
+  }
+}
+
 template <int ES, int D>
 struct DecodeShape {
   static constexpr int E = 16 / ES;                // elements per granule
@@ -330,7 +443,10 @@ struct DecodeShape {
   static constexpr int VG = BS * D * ES / 16 / 64; // V granules per lane per block
   static constexpr int DPL = D / 64;               // d values per lane
   static constexpr int TILE = BS * D * ES;         // bytes of one K or V tile
-  static constexpr int QROW = KH * 16 + 16;        // LDS bytes of a padded half q row
+  static constexpr int QES = ES == 4 ? 4 : 2;      // query element bytes (bf16 for fp8 caches)
+  static constexpr int QKG = D * QES / 16;         // 16-byte granules per q row
+  static constexpr int QKH = QKG / 2;              // per half row
+  static constexpr int QROW = QKH * 16 + 16;       // LDS bytes of a padded half q row
 };
 
 template <int ES, int D>
@@ -776,7 +892,7 @@ __device__ __forceinline__ void stream_merge(const StreamParams& sp, int wA, int
         for (int j = 0; j < DPL; ++j) num[j] = fmaf(wk, a[g][k][j], num[j]);
       }
 #pragma unroll
-      for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+      for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den * sp.d.out_scale;
     }
     return;
   }
@@ -832,7 +948,7 @@ __device__ __forceinline__ void stream_merge(const StreamParams& sp, int wA, int
     }
     den = wave_sum(den);
 #pragma unroll
-    for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den;
+    for (int j = 0; j < DPL; ++j) o[g * D + j * 64 + lane] = num[j] / den * sp.d.out_scale;
   }
 }
 
@@ -841,7 +957,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     StreamParams sp) {
   using S = DecodeShape<ES, D>;
   constexpr int QBUF = StreamLds<ES, D, G>::QBUF;
-  constexpr int QGR = G * S::KG;             // 16-byte granules of one item's q rows
+  constexpr int QGR = G * S::QKG;            // 16-byte granules of one item's q rows
   constexpr int NQ = (QGR + 63) / 64;        // per lane
   __shared__ __align__(16) char q_lds[QBUF];
   __shared__ __align__(16) float p_lds[32 * G];
@@ -1018,7 +1134,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   };
   auto load_q = [&](uint4 (&qr)[NQ], const StreamCur& c) {
     const uint4* src = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(p.q) + ((size_t)c.row * hq + (size_t)c.h * G) * D * ES);
+        static_cast<const char*>(p.q) + ((size_t)c.row * hq + (size_t)c.h * G) * D * S::QES);
 #pragma unroll
     for (int i = 0; i < NQ; ++i) {
       const int gi = lane + 64 * i;
@@ -1030,8 +1146,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int i = 0; i < NQ; ++i) {
       const int gi = lane + 64 * i;
       if (gi < QGR) {
-        const int g = gi / S::KG, c = gi % S::KG;
-        const int hh = c / S::KH, cc = c % S::KH;
+        const int g = gi / S::QKG, c = gi % S::QKG;
+        const int hh = c / S::QKH, cc = c % S::QKH;
         *reinterpret_cast<uint4*>(q_lds + (g * 2 + hh) * S::QROW + cc * 16) = qr[i];
       }
     }
@@ -1071,6 +1187,33 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
     const char* qh = q_lds + half * S::QROW;
+    if constexpr (ES == 1) {
+      // K granule cc holds 16 E4M3 codes (d = 16 cc .. of this half row),
+      // converted pairwise to bf16 (exact) for v_dot2 against two q granules
+#pragma unroll
+      for (int cc = 0; cc < S::KH; ++cc) {
+        const uint4 kg = r.k[cc];
+        const uint32_t kw[4] = {kg.x, kg.y, kg.z, kg.w};
+        uint32_t kb[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          kb[2 * q] = fp8x2_bf16<false>(kw[q]);
+          kb[2 * q + 1] = fp8x2_bf16<true>(kw[q]);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint4 q0 = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + (2 * cc) * 16);
+          const uint4 q1 = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + (2 * cc + 1) * 16);
+          const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[e]),
+                                                    __builtin_bit_cast(bf16x2_t, kb[e]), sc[g], false);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
+      }
+    } else {
     uint4 qcur[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) qcur[g] = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW);
@@ -1105,6 +1248,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
       for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
     }
+    }
     const int tok0 = c.j * 32;
     const bool tok_ok = tok0 + (lane >> 1) < c.L;
 #pragma unroll
@@ -1129,10 +1273,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb) {
       const int valid = c.L - (tok0 + jb * BS);
-      if (valid >= BS)
-        pv_block<ES, D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
-      else if (valid > 0)
-        pv_block<ES, D, G, true>(r.v[jb], p_lds, jb * BS, valid, acc);
+      if constexpr (ES == 1) {
+        if (valid >= BS)
+          pv_block_fp8<D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
+        else if (valid > 0)
+          pv_block_fp8<D, G, true>(r.v[jb], p_lds, jb * BS, valid, acc);
+      } else {
+        if (valid >= BS)
+          pv_block<ES, D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
+        else if (valid > 0)
+          pv_block<ES, D, G, true>(r.v[jb], p_lds, jb * BS, valid, acc);
+      }
     }
     wave_sync();
   };
@@ -1156,7 +1307,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < S::DPL; ++j) o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g];
+        for (int j = 0; j < S::DPL; ++j)
+          o[g * D + j * 64 + lane] = acc[g][j] / l_tot[g] * p.out_scale;
       reset_state();
       return;
     }
@@ -1309,6 +1461,7 @@ static DecodeParams make_decode_params(const CacheDesc& c, const AttnDesc& a) {
   p.qsl = a.query_start_loc;
   p.num_seqs = a.num_seqs;
   p.scale_log2 = a.scale * kLog2e;
+  p.out_scale = a.out_scale;
   p.ws_acc = a.ws_acc;
   p.ws_ml = a.ws_ml;
   p.full_units = (int)a.full_units;
@@ -1356,7 +1509,9 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
     case 4: nb = stream_blocks_per_cu<ES_, D_, 4>(); break; \
     case 8: nb = stream_blocks_per_cu<ES_, D_, 8>(); break; \
   }
-  if (dtype_bytes == 4 && D == 64) { PKV_SLOTS(4, 64) }
+  if (dtype_bytes == 1 && D == 64) { PKV_SLOTS(1, 64) }
+  else if (dtype_bytes == 1 && D == 128) { PKV_SLOTS(1, 128) }
+  else if (dtype_bytes == 4 && D == 64) { PKV_SLOTS(4, 64) }
   else if (dtype_bytes == 4 && D == 128) { PKV_SLOTS(4, 128) }
   else if (dtype_bytes == 2 && D == 64) { PKV_SLOTS(2, 64) }
   else if (dtype_bytes == 2 && D == 128) { PKV_SLOTS(2, 128) }
@@ -1378,7 +1533,10 @@ static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hi
   sp.part_acc = a.stream_acc;
   sp.part_ml = a.stream_ml;
   const int G = a.hq / c.hkv;
-  if (c.dtype_bytes == 4) {
+  if (c.dtype_bytes == 1) {
+    if (c.head_size == 64) return stream_g<1, 64>(G, sp, stream);
+    if (c.head_size == 128) return stream_g<1, 128>(G, sp, stream);
+  } else if (c.dtype_bytes == 4) {
     if (c.head_size == 64) return stream_g<4, 64>(G, sp, stream);
     if (c.head_size == 128) return stream_g<4, 128>(G, sp, stream);
   } else {
@@ -1391,6 +1549,7 @@ static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hi
 hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   const DecodeParams p = make_decode_params(c, a);
   if (a.stream_waves > 0) return launch_decode_stream(c, a, stream);
+  if (c.fp8) return hipErrorInvalidValue;  // fp8 caches are read by the stream kernel only
   const int G = a.hq / c.hkv;
   if (c.dtype_bytes == 4) {
     if (c.head_size == 64) return decode_rows_g<4, 64>(G, p, a.decode_units, a.num_seqs, c.hkv, stream);

@@ -16,8 +16,9 @@ import torch
 
 from . import _lib as L
 
-_CODE_TORCH = {2: torch.int16, 4: torch.int32}
-_CODE_NP = {2: np.int16, 4: np.int32}
+_CODE_TORCH = {1: torch.uint8, 2: torch.int16, 4: torch.int32}
+_CODE_NP = {1: np.uint8, 2: np.int16, 4: np.int32}
+_DTYPE = {"f32": L.PKV_F32, "bf16": L.PKV_BF16, "fp8": L.PKV_FP8_E4M3}
 
 
 def _dev_codes(a: np.ndarray, es: int, device) -> torch.Tensor:
@@ -31,17 +32,22 @@ class PagedStep:
     def __init__(self, w, device: str = "cuda"):
         self.w = w
         self.device = torch.device(device)
-        self.es = w.dtype_bytes
-        self.dtype = L.PKV_F32 if w.dtype == "f32" else L.PKV_BF16
+        kv_dtype = getattr(w, "kv_dtype", w.dtype)
+        self.es = {"f32": 4, "bf16": 2, "fp8": 1}[kv_dtype]   # cache element bytes
+        self.in_es = w.dtype_bytes                           # new rows and queries
+        self.dtype = _DTYPE[kv_dtype]
         self.block_bytes = 2 * 16 * w.num_kv_heads * w.head_size * self.es
         nbytes = w.num_blocks * self.block_bytes
         self.kv = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         fill = int(w.pool_fill)
-        if self.es == 2:
+        if self.es == 1:
+            self.kv.fill_(fill)
+        elif self.es == 2:
             self.kv.view(torch.int16).fill_(fill - (1 << 16) if fill >= 1 << 15 else fill)
         else:
             self.kv.view(torch.int32).fill_(fill - (1 << 32) if fill >= 1 << 31 else fill)
-        self.cache = L.Cache(self.kv, w.num_blocks, w.num_kv_heads, w.head_size, self.dtype)
+        self.cache = L.Cache(self.kv, w.num_blocks, w.num_kv_heads, w.head_size, self.dtype,
+                             k_scale=getattr(w, "k_scale", 1.0), v_scale=getattr(w, "v_scale", 1.0))
         assert L.pkv_block_bytes(self.cache.desc) == self.block_bytes
         self.pool = L.Pool(w.num_blocks, w.free_order)
         self.max_blocks = max(1, int(-(-int(w.seq_lens.max()) // 16)))
@@ -80,8 +86,8 @@ class PagedStep:
                 self.pool.release(t, -(-int(w.prompt_len[p]) // 16))
         slots = np.concatenate(slots_all) if slots_all else np.zeros(0, np.int64)
         if slots.size:
-            k = _dev_codes(np.concatenate(k_parts), self.es, self.device)
-            v = _dev_codes(np.concatenate(v_parts), self.es, self.device)
+            k = _dev_codes(np.concatenate(k_parts), self.in_es, self.device)
+            v = _dev_codes(np.concatenate(v_parts), self.in_es, self.device)
             s_dev = torch.from_numpy(slots).to(self.device)
             L.paged_kv_write(self.cache, k, v, s_dev)
 
@@ -106,9 +112,9 @@ class PagedStep:
         self.block_tables = torch.from_numpy(self.tables).to(d)
         self.seq_lens = torch.from_numpy(self.h_seq_lens).to(d)
         self.qsl = torch.from_numpy(self.h_qsl).to(d)
-        self.k_new = _dev_codes(w.new_k, self.es, d)
-        self.v_new = _dev_codes(w.new_v, self.es, d)
-        self.q = _dev_codes(w.q, self.es, d)
+        self.k_new = _dev_codes(w.new_k, self.in_es, d)
+        self.v_new = _dev_codes(w.new_v, self.in_es, d)
+        self.q = _dev_codes(w.q, self.in_es, d)
         self.out = torch.zeros((w.num_tokens, w.num_q_heads, w.head_size), dtype=torch.float32,
                                device=d)
         self.decode_only = bool(np.all(w.q_len == 1))
@@ -140,7 +146,7 @@ class PagedStep:
     def pool_codes(self) -> np.ndarray:
         """The whole pool as codes [num_blocks][Hkv][2][16*D] on the host."""
         w = self.w
-        a = self.kv.cpu().numpy().view(np.uint16 if self.es == 2 else np.uint32)
+        a = self.kv.cpu().numpy().view({1: np.uint8, 2: np.uint16, 4: np.uint32}[self.es])
         return a.reshape(w.num_blocks, w.num_kv_heads, 2, 16 * w.head_size)
 
 

@@ -288,3 +288,59 @@ def test_prefill_chunk_rows_dense_sample():
     ref = scenario.sequence_attention(w, s, rows)
     got = out[int(w.query_start_loc[s]) + np.asarray(rows)]
     _check_attention(got, ref, "bf16", "prefill chunk rows")
+
+
+# ------------------------------------------------------------- FP8 KV cache
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_fp8_small_workload_full_parity(cfg):
+    """FP8 E4M3 cache: quantized writes give the oracle's pool bit for bit
+    (every code and untouched byte), attention within the bars."""
+    w = workloads.make_fp8(cfg, small_size=True)
+    _announce(f"fp8 small config {cfg}: B={w.batch} L={w.seq_lens.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"]), "fp8 pool differs from the oracle's"
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"fp8 small config {cfg}")
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_fp8_full_size_sampled_parity(cfg):
+    w = workloads.make_fp8(cfg)
+    _announce(f"fp8 full config {cfg}: B={w.batch} blocks={w.num_blocks}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rows = _sample_seqs(w)
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in rows])
+    got = np.concatenate([out[s:s + 1] for s in rows])
+    _check_attention(got, want, "bf16", f"fp8 full config {cfg}")
+
+
+def test_fp8_every_code_decodes_exactly():
+    """One token per sequence (its own, written this step): the output is
+    that token's V times the V scale, exactly.  V holds every E4M3 code once
+    (bf16 inputs equal to code value * scale, which quantize to the code);
+    the stored bytes and the outputs are checked bit for bit."""
+    streams = [np.random.default_rng(x) for x in (51, 52, 53, 54)]
+    w = workloads._build(3, "fp8 codes", "bf16", 2, 2, 128, 128 ** -0.5, np.zeros(1, np.int32),
+                         np.ones(1, np.int32), 4, streams)
+    w.cache_dtype, w.k_scale, w.v_scale, w.pool_fill = "fp8", 0.5, 1.0 / 64, workloads.FP8_NAN
+    table = po.e4m3_table()
+    vals = (table * w.v_scale).astype(np.float32)              # exact in bf16 (4 significant bits)
+    codes = np.arange(256).reshape(2, 128)
+    w.new_v = workloads._bf16_codes(np.nan_to_num(vals, nan=0.0)[codes][None])
+    nan = np.isnan(vals[codes])                                # codes 0x7F and 0xFF
+    w.new_v[0][nan] = 0x7FC0 | ((codes[nan] & 0x80) << 8)      # NaN inputs with their sign
+    w.new_k = np.zeros_like(w.new_v)
+    _announce("fp8 every code")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"])
+    blk = int(st.tables[0, 0])
+    vt = st.pool_codes()[blk, :, 1].reshape(2, 128, 16)[:, :, 0]   # V of token 0, every d
+    assert np.array_equal(vt, codes.astype(np.uint8)), "written codes"
+    out = st.out.cpu().numpy()[0]                              # [Hq=2][128]
+    want = vals[codes]
+    assert np.array_equal(np.isnan(out), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(out[ok], want[ok]), "decoded values"

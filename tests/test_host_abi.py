@@ -41,6 +41,29 @@ def test_block_bytes_per_config(cfg):
     assert P.pkv_block_bytes(d) == po.block_bytes(16, w.num_kv_heads, w.head_size, w.dtype_bytes)
 
 
+def test_fp8_descriptor_bytes_and_scales():
+    """An FP8 E4M3 cache has one byte per element; its scales must be finite
+    and positive."""
+    d = P.descriptor(7, 8, 128, P.PKV_FP8_E4M3, k_scale=0.5, v_scale=0.25)
+    assert P.pkv_block_bytes(d) == po.block_bytes(16, 8, 128, 1) == 32768
+    good = P.descriptor(16, 8, 128, P.PKV_FP8_E4M3, kv_ptr=0x1000, k_scale=0.5, v_scale=0.5)
+    assert _call_decode(good, hq=32) == 4                       # gets to the workspace check
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (float("nan"), 1.0)):
+        bad = P.descriptor(16, 8, 128, P.PKV_FP8_E4M3, kv_ptr=0x1000, k_scale=ks, v_scale=vs)
+        assert _call_decode(bad, hq=32) == 7                    # PKV_ERR_RANGE
+
+
+def test_fp8_cache_rejects_prefill_rows():
+    """Rows with q_len > 1 need a bf16 cache."""
+    d = P.descriptor(64, 8, 128, P.PKV_FP8_E4M3, kv_ptr=0x1000, k_scale=0.5, v_scale=0.5)
+    qsl = np.array([0, 1, 5], np.int32)
+    sl = np.array([3, 9], np.int32)
+    st = L._c["paged_attention_mixed"](
+        ctypes.byref(d), 1, 1, 32, 1, 1, qsl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        sl.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 4, 2, 5, 0.1, 1, 1 << 30, None)
+    assert st == 3                                              # PKV_ERR_DTYPE
+
+
 def test_block_bytes_rejects_bad_descriptors():
     assert P.pkv_block_bytes(P.descriptor(7, 8, 96, P.PKV_BF16)) == 0     # head size
     assert P.pkv_block_bytes(P.descriptor(7, 8, 128, 9)) == 0             # dtype
