@@ -32,14 +32,17 @@ METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batc
 # of k_decode_stream; see profiles/decode_8b_gqa_b256_traffic.md.  Reset to
 # None whenever the kernel changes until the counters are taken again.
 MEASURED_TRAFFIC_BYTES = 1_351_737_000
+# The same for the FP8 E4M3 cache variant (k_decode_stream<1,128,4>); see
+# profiles/decode_8b_gqa_b256_fp8_kv.md.
+MEASURED_TRAFFIC_BYTES_FP8 = 692_397_000
 
 
 def algorithmic_bytes(w) -> int:
     """Bytes the decode step must move: K and V of every valid token of every
-    kv head, the query rows read, the fp32 outputs written, the block-table
-    entries in use and the lengths."""
+    kv head (at the cache's element size), the query rows read, the fp32
+    outputs written, the block-table entries in use and the lengths."""
     L = w.seq_lens.astype(np.int64)
-    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * w.dtype_bytes
+    kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * w.kv_dtype_bytes
     q = w.batch * w.num_q_heads * w.head_size * w.dtype_bytes
     out = w.batch * w.num_q_heads * w.head_size * 4
     tables = int(((L + 15) // 16).sum()) * 4
@@ -170,9 +173,10 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["decode", "mixed"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8"], default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
-                         "prefill step (reported separately)")
+                         "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
+                         "cache (both reported separately)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MiB of scratch between timed steps (0 = back to back)")
@@ -195,7 +199,8 @@ def main() -> None:
         print(json.dumps(run_mixed(args)), flush=True)
         return
 
-    w = workloads.make(3)
+    fp8 = args.workload == "decode-fp8"
+    w = workloads.make_fp8(3) if fp8 else workloads.make(3)
     st = gpu_step.PagedStep(w, "cuda")
     st.build_history()
     st.prepare_step()
@@ -232,7 +237,8 @@ def main() -> None:
     value = w.batch / (ms_per_step * 1e-3)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if not fp8 else
+        "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256, FP8 KV cache",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -242,12 +248,13 @@ def main() -> None:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 cache, bf16 q, f32 accumulate" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
             "workload": "Llama-3-8B-shaped GQA decode: 32 q / 8 kv heads, head 128, bf16 "
                         "N(0,1), batch 256, lognormal contexts (median 800, sigma 1, "
-                        "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool",
+                        "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool"
+                        + (", KV cache FP8 E4M3 with K/V scales 1/64" if fp8 else ""),
             "global_batch": w.batch,
             "sum_context_tokens": int(w.seq_lens.sum()),
             "parallelism": "none (1 GPU)",
@@ -266,11 +273,11 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": MEASURED_TRAFFIC_BYTES,
+            "traffic": MEASURED_TRAFFIC_BYTES_FP8 if fp8 else MEASURED_TRAFFIC_BYTES,
             "kernel": "paged_attention_decode (k_decode_stream, one launch)",
             "algorithmic_bytes_per_launch": alg,
         },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(w),
+        "cpu_baseline": None if (args.no_cpu_baseline or fp8) else cpu_baseline(w),
     }
     print(json.dumps(rec), flush=True)
 

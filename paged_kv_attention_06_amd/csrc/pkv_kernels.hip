@@ -60,10 +60,15 @@ __device__ __forceinline__ uint32_t e4m3_code(float y, uint32_t sign) {
 }
 
 typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 // Two E4M3 codes (bytes 2 HI, 2 HI + 1 of w) -> two floats / two bf16.
 template <bool HI>
 __device__ __forceinline__ f32x2v_t fp8x2_f32(uint32_t w) {
   return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_f16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI));
 }
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t w) {
@@ -408,29 +413,36 @@ __device__ __forceinline__ void pv_block(const uint4 (&vr)[BS * D * ES / 16 / 64
 }
 
 // P.V over one block of an fp8 cache: vr[dd] holds the 16 keys' E4M3 codes
-// of d = 64 dd + lane (one granule per d), converted two at a time.
+// of d = 64 dd + lane (one granule per d).  Codes become fp16 pairs (exact)
+// and meet the probabilities, stored in LDS as fp16 [head][32 keys of the
+// step], in v_dot2_f32_f16.  Keys at or past `valid_keys` get a zero value,
+// so unwritten slots (any bits, NaN included) cannot reach the sums.
 template <int D, int G, bool CHECK>
-__device__ __forceinline__ void pv_block_fp8(const uint4 (&vr)[D / 64], const float* __restrict__ p_lds,
+__device__ __forceinline__ void pv_block_fp8(const uint4 (&vr)[D / 64], const uint16_t* __restrict__ p16,
                                              int key_base, int valid_keys, float (&acc)[G][D / 64]) {
   constexpr int DPL = D / 64;
-  float pk[16][G];
+  uint32_t pp[G][8];  // probability pairs (keys 2q, 2q + 1) of each head
 #pragma unroll
-  for (int e = 0; e < 16; ++e)
-#pragma unroll
-    for (int g = 0; g < G; ++g) pk[e][g] = p_lds[(key_base + e) * G + g];
+  for (int g = 0; g < G; ++g) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p16 + g * 32 + key_base);
+    const uint4 b = *reinterpret_cast<const uint4*>(p16 + g * 32 + key_base + 8);
+    pp[g][0] = a.x; pp[g][1] = a.y; pp[g][2] = a.z; pp[g][3] = a.w;
+    pp[g][4] = b.x; pp[g][5] = b.y; pp[g][6] = b.z; pp[g][7] = b.w;
+  }
 #pragma unroll
   for (int dd = 0; dd < DPL; ++dd) {
     const uint32_t w[4] = {vr[dd].x, vr[dd].y, vr[dd].z, vr[dd].w};
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const f32x2v_t v = (q & 1) ? fp8x2_f32<true>(w[q >> 1]) : fp8x2_f32<false>(w[q >> 1]);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int e = 2 * q + k;
-        if (CHECK && e >= valid_keys) continue;
-#pragma unroll
-        for (int g = 0; g < G; ++g) acc[g][dd] = fmaf(pk[e][g], v[k], acc[g][dd]);
+      uint32_t v = (q & 1) ? fp8x2_f16<true>(w[q >> 1]) : fp8x2_f16<false>(w[q >> 1]);
+      if (CHECK) {
+        if (2 * q >= valid_keys) v = 0u;
+        else if (2 * q + 1 >= valid_keys) v &= 0xFFFFu;
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        acc[g][dd] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pp[g][q]),
+                                            __builtin_bit_cast(f16x2_t, v), acc[g][dd], false);
     }
   }
 }
@@ -1265,8 +1277,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
       }
       const float pr = __builtin_amdgcn_exp2f(x - m_run[g]);
       if (half == 0) {
-        l_lane[g] += pr;
-        p_lds[(lane >> 1) * G + g] = pr;
+        if constexpr (ES == 1) {  // fp16 probabilities; the sums use the same rounded values
+          const _Float16 ph = (_Float16)pr;
+          l_lane[g] += (float)ph;
+          reinterpret_cast<_Float16*>(p_lds)[g * 32 + (lane >> 1)] = ph;
+        } else {
+          l_lane[g] += pr;
+          p_lds[(lane >> 1) * G + g] = pr;
+        }
       }
     }
     wave_sync();
@@ -1274,10 +1292,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     for (int jb = 0; jb < 2; ++jb) {
       const int valid = c.L - (tok0 + jb * BS);
       if constexpr (ES == 1) {
+        const uint16_t* p16 = reinterpret_cast<const uint16_t*>(p_lds);
         if (valid >= BS)
-          pv_block_fp8<D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
+          pv_block_fp8<D, G, false>(r.v[jb], p16, jb * BS, BS, acc);
         else if (valid > 0)
-          pv_block_fp8<D, G, true>(r.v[jb], p_lds, jb * BS, valid, acc);
+          pv_block_fp8<D, G, true>(r.v[jb], p16, jb * BS, valid, acc);
       } else {
         if (valid >= BS)
           pv_block<ES, D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
@@ -1516,10 +1535,13 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
   else if (dtype_bytes == 2 && D == 64) { PKV_SLOTS(2, 64) }
   else if (dtype_bytes == 2 && D == 128) { PKV_SLOTS(2, 128) }
 #undef PKV_SLOTS
-  // One wave per SIMD.  Measured on MI355X (8B GQA batch 256): 0.260 ms
-  // against 0.269 ms with two waves per SIMD, whose extra requests in flight
-  // HBM does not serve any faster.
-  return (nb < 4 ? nb : 4) * cus;
+  // bf16 / fp32 caches: one wave per SIMD.  Measured on MI355X (8B GQA batch
+  // 256): 0.260 ms against 0.269 ms with two waves per SIMD, whose extra
+  // requests in flight HBM does not serve any faster.  fp8 caches move half
+  // the bytes per step for more arithmetic: two waves per SIMD hide each
+  // step's chain (0.157 ms against 0.208 with one and 0.166 with three).
+  const int per_cu = dtype_bytes == 1 ? 8 : 4;
+  return (nb < per_cu ? nb : per_cu) * cus;
 }
 
 static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
@@ -1597,7 +1619,6 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
