@@ -43,10 +43,11 @@ def algorithmic_bytes(w) -> int:
     outputs written, the block-table entries in use and the lengths."""
     L = w.seq_lens.astype(np.int64)
     kv = int(L.sum()) * 2 * w.num_kv_heads * w.head_size * w.kv_dtype_bytes
-    q = w.batch * w.num_q_heads * w.head_size * w.dtype_bytes
-    out = w.batch * w.num_q_heads * w.head_size * 4
+    q = w.num_tokens * w.num_q_heads * w.head_size * w.dtype_bytes
+    out = w.num_tokens * w.num_q_heads * w.head_size * 4
     tables = int(((L + 15) // 16).sum()) * 4
-    return kv + q + out + tables + 4 * w.batch
+    qsl = 4 * (w.batch + 1) if w.num_tokens != w.batch else 0
+    return kv + q + out + tables + 4 * w.batch + qsl
 
 
 def cpu_baseline(w, min_s: float = 10.0):
@@ -173,10 +174,13 @@ def main() -> None:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify"],
+                    default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
                          "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
-                         "cache (both reported separately)")
+                         "cache; verify: the same batch querying k + 1 = 4 positions per "
+                         "sequence (speculative decoding); all but decode are reported "
+                         "separately")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mb", type=int, default=0,
                     help="write this many MiB of scratch between timed steps (0 = back to back)")
@@ -200,7 +204,8 @@ def main() -> None:
         return
 
     fp8 = args.workload == "decode-fp8"
-    w = workloads.make_fp8(3) if fp8 else workloads.make(3)
+    verify = args.workload == "verify"
+    w = workloads.make_fp8(3) if fp8 else (workloads.make_verify() if verify else workloads.make(3))
     st = gpu_step.PagedStep(w, "cuda")
     st.build_history()
     st.prepare_step()
@@ -234,11 +239,12 @@ def main() -> None:
     attn_mean = float(attn_ms.mean())
     alg = algorithmic_bytes(w)
     achieved = alg / (attn_mean * 1e-3) / 1e9
-    value = w.batch / (ms_per_step * 1e-3)
+    value = w.num_tokens / (ms_per_step * 1e-3)
 
     rec = {
-        "metric": METRIC if not fp8 else
-        "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256, FP8 KV cache",
+        "metric": (METRIC if not (fp8 or verify) else
+                   "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256, "
+                   + ("FP8 KV cache" if fp8 else "speculative verify, 4 query rows per sequence")),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -254,7 +260,9 @@ def main() -> None:
             "workload": "Llama-3-8B-shaped GQA decode: 32 q / 8 kv heads, head 128, bf16 "
                         "N(0,1), batch 256, lognormal contexts (median 800, sigma 1, "
                         "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool"
-                        + (", KV cache FP8 E4M3 with K/V scales 1/64" if fp8 else ""),
+                        + (", KV cache FP8 E4M3 with K/V scales 1/64" if fp8 else "")
+                        + (", each sequence appends and queries its last token plus 3 draft "
+                           "tokens (causal)" if verify else ""),
             "global_batch": w.batch,
             "sum_context_tokens": int(w.seq_lens.sum()),
             "parallelism": "none (1 GPU)",
@@ -273,11 +281,13 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": MEASURED_TRAFFIC_BYTES_FP8 if fp8 else MEASURED_TRAFFIC_BYTES,
-            "kernel": "paged_attention_decode (k_decode_stream, one launch)",
+            "traffic": None if verify else (MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
+                                            MEASURED_TRAFFIC_BYTES),
+            "kernel": ("paged_attention_mixed (k_v_fp16 + k_prefill_tile)" if verify else
+                       "paged_attention_decode (k_decode_stream, one launch)"),
             "algorithmic_bytes_per_launch": alg,
         },
-        "cpu_baseline": None if (args.no_cpu_baseline or fp8) else cpu_baseline(w),
+        "cpu_baseline": None if (args.no_cpu_baseline or fp8 or verify) else cpu_baseline(w),
     }
     print(json.dumps(rec), flush=True)
 

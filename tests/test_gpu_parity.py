@@ -344,3 +344,27 @@ def test_fp8_every_code_decodes_exactly():
     assert np.array_equal(np.isnan(out), np.isnan(want))
     ok = ~np.isnan(want)
     assert np.array_equal(out[ok], want[ok]), "decoded values"
+
+
+# ------------------------------------------------- speculative verify (q_len = k + 1)
+def test_verify_small_full_parity():
+    """Each sequence queries its last token and 3 draft tokens, causally."""
+    w = workloads.make_verify(small_size=True)
+    _announce(f"verify small: L={w.seq_lens.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"])
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", "verify small")
+
+
+def test_verify_full_size_sampled_parity():
+    w = workloads.make_verify()
+    _announce(f"verify full: B={w.batch} T={w.num_tokens}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    qsl = w.query_start_loc
+    seqs = _sample_seqs(w)
+    got = np.concatenate([out[qsl[s]:qsl[s + 1]] for s in seqs])
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in seqs])
+    _check_attention(got, want, "bf16", "verify full")

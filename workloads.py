@@ -168,6 +168,28 @@ def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, sca
     return w
 
 
+def make_verify(k: int = 3, seed: int = 0, small_size: bool = False) -> Workload:
+    """Speculative-decoding verify step on the 8B GQA decode batch: every
+    sequence appends its last accepted token plus k draft tokens and queries
+    all k + 1 positions (causal), as the pages' verify pass does (k = 3 in
+    their n-gram example).  Lengths, pool and values are drawn like config
+    3 (batch 256, or 12 short sequences with small_size)."""
+    streams = [np.random.default_rng(x)
+               for x in np.random.SeedSequence(20_000 + 1000 * seed + 10 * small_size).spawn(4)]
+    r_len = streams[0]
+    if small_size:
+        B = 12
+        L = np.clip(np.rint(r_len.lognormal(np.log(120.0), 1.0, size=B)), k + 1, 900).astype(np.int32)
+        L[0], L[1], L[2] = k + 1, 16, 17
+        pool = 4000
+    else:
+        B = 256
+        L = np.clip(np.rint(r_len.lognormal(np.log(800.0), 1.0, size=B)), 16, 8192).astype(np.int32)
+        pool = 200_000
+    return _build(3, f"8B GQA verify (k={k})" + (" (small)" if small_size else ""), "bf16", 32, 8,
+                  128, 128 ** -0.5, L - (k + 1), np.full(B, k + 1, np.int32), pool, streams)
+
+
 def make_fp8(config_id: int, seed: int = 0, small_size: bool = False) -> Workload:
     """A bf16 workload (configs 2, 3 or 5, full or small) whose KV cache is
     FP8 E4M3 with K and V scales of 1/64: same lengths, blocks and drawn
