@@ -169,12 +169,60 @@ def run_mixed(args):
     }
 
 
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
+
+
+def run_swap(args):
+    """Swap preemption's data move: all blocks of the 32 longest sequences of
+    the 8B GQA decode batch go out to pinned host memory and come back."""
+    import torch
+
+    import workloads
+    from paged_kv_attention_06_amd import _lib as L
+    from paged_kv_attention_06_amd import step as gpu_step
+
+    w = workloads.make(3)
+    st = gpu_step.PagedStep(w, "cuda")
+    st.build_history()
+    st.prepare_step()
+    torch.cuda.synchronize()
+    longest = np.argsort(-w.seq_lens)[:32]
+    blocks = [int(b) for s in longest for b in st.tables[s][:-(-int(w.seq_lens[s]) // 16)]]
+    n = len(blocks)
+    host = torch.empty(n * st.block_bytes, dtype=torch.uint8, pin_memory=True)
+    used = {int(b) for s in range(w.batch) for b in st.tables[s][:-(-int(w.seq_lens[s]) // 16)]}
+    fresh = [b for b in range(w.num_blocks) if b not in used][:n]
+    out_pairs = torch.tensor([[b, i] for i, b in enumerate(blocks)], dtype=torch.int64).cuda()
+    in_pairs = torch.tensor([[i, b] for i, b in enumerate(fresh)], dtype=torch.int64).cuda()
+    stream = torch.cuda.current_stream()
+    t_out = _timed(lambda: L.block_swap(st.cache, host, out_pairs, True), args.steps,
+                   args.warmup, stream)
+    t_in = _timed(lambda: L.block_swap(st.cache, host, in_pairs, False), args.steps,
+                  args.warmup, stream)
+    nbytes = n * st.block_bytes
+    gb_out = nbytes / (float(t_out.mean()) * 1e-3) / 1e9
+    gb_in = nbytes / (float(t_in.mean()) * 1e-3) / 1e9
+    return {
+        "metric": "block swap GB/s over the host link (swap out / swap in)",
+        "value": gb_out, "unit": "GB/s", "higher_is_better": True, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": float(t_out.mean()),
+        "dtype": "bytes", "data": "synthetic",
+        "config": {"workload": f"8B GQA pool (64 KiB blocks): all {n} blocks of the 32 longest "
+                               f"sequences ({nbytes / 2**20:.0f} MiB) to pinned host memory and back"},
+        "swap_out_ms": float(t_out.mean()), "swap_in_ms": float(t_in.mean()),
+        "swap_out_gbps": gb_out, "swap_in_gbps": gb_in,
+        "roofline": {"bound": "host link", "achieved": gb_out, "peak": HOST_LINK_PEAK_GBPS,
+                     "unit": "GB/s", "frac": gb_out / HOST_LINK_PEAK_GBPS, "traffic": None,
+                     "kernel": "block_swap (k_block_swap)", "algorithmic_bytes_per_launch": nbytes},
+    }
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify"],
+    ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify", "swap"],
                     default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
                          "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
@@ -201,6 +249,9 @@ def main() -> None:
 
     if args.workload == "mixed":
         print(json.dumps(run_mixed(args)), flush=True)
+        return
+    if args.workload == "swap":
+        print(json.dumps(run_swap(args)), flush=True)
         return
 
     fp8 = args.workload == "decode-fp8"

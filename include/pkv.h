@@ -133,6 +133,26 @@ int paged_kv_write(const pkv_cache* cache, const void* k_new, const void* v_new,
  * repeat).  num_pairs == 0 is a no-op. */
 int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, void* stream);
 
+/* ---------------------------------------------------- block swap (host) */
+enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 };
+
+/* Swap preemption's data move (juhe.plus section 3.9: a preempted
+ * sequence's blocks are copied to CPU memory over PCIe and copied back when
+ * it resumes; Continuous batching + PagedAttention, swap vs recompute):
+ * whole blocks (K and V of all kv heads, pkv_block_bytes each) move between
+ * the device pool and a host pool with the same block size.
+ *   host_kv    host [num_host_blocks][pkv_block_bytes(cache)], pinned and
+ *              device-mapped (hipHostMalloc / torch pin_memory); other memory
+ *              is rejected with PKV_ERR_RANGE
+ *   pairs      device int64 [num_pairs][2] = (src, dst): a device block id and
+ *              a host block id for PKV_SWAP_OUT, the reverse for PKV_SWAP_IN
+ *   direction  PKV_SWAP_OUT or PKV_SWAP_IN
+ * Preconditions on device data: ids in range; dsts distinct.  The copy is
+ * asynchronous on `stream` (host memory is final after the stream syncs).
+ * num_pairs == 0 is a no-op. */
+int block_swap(const pkv_cache* cache, void* host_kv, int64_t num_host_blocks,
+               const int64_t* pairs, int64_t num_pairs, int32_t direction, void* stream);
+
 /* ------------------------------------------------------------ attention */
 /* Workspace bytes paged_attention_decode / paged_attention_mixed need for
  * these host lengths: the split-K partials of decode rows (per split row:

@@ -292,6 +292,17 @@ def block_copy(pool: np.ndarray, pairs) -> None:
         pool[int(d)] = snapshot[int(s)]
 
 
+def block_swap(dev_pool: np.ndarray, host_pool: np.ndarray, pairs, to_host: bool) -> None:
+    """Swap preemption's data move (juhe.plus 3.9; vLLM 源码精读 on swap out
+    to CPU memory and back): every (src, dst) pair copies a whole block from
+    the device pool to the host pool (to_host) or back.  Reads see the
+    contents before the call."""
+    src_pool, dst_pool = (dev_pool, host_pool) if to_host else (host_pool, dev_pool)
+    snapshot = {int(s): src_pool[int(s)].copy() for s, _ in pairs}
+    for s, d in pairs:
+        dst_pool[int(d)] = snapshot[int(s)]
+
+
 # ----------------------------------------------------------------------------
 # attention
 # ----------------------------------------------------------------------------

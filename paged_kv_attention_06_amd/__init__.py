@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     PkvError,
     Pool,
     block_copy,
+    block_swap,
     descriptor,
     paged_attention_decode,
     paged_attention_mixed,

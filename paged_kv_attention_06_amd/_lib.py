@@ -56,6 +56,9 @@ _c["paged_kv_write"] = _sig("paged_kv_write", ctypes.c_int,
                             [ctypes.POINTER(PkvCache), _vp, _vp, _vp, ctypes.c_int64, _vp])
 _c["block_copy"] = _sig("block_copy", ctypes.c_int,
                         [ctypes.POINTER(PkvCache), _vp, ctypes.c_int64, _vp])
+_c["block_swap"] = _sig("block_swap", ctypes.c_int,
+                        [ctypes.POINTER(PkvCache), _vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                         ctypes.c_int32, _vp])
 _c["pkv_attention_workspace_bytes"] = _sig("pkv_attention_workspace_bytes", ctypes.c_size_t,
                                            [ctypes.POINTER(PkvCache), ctypes.c_int32, _i32p,
                                             _i32p, ctypes.c_int32])
@@ -178,6 +181,19 @@ def paged_kv_write(cache: Cache, k_new, v_new, slot_mapping, stream=None) -> Non
 def block_copy(cache: Cache, pairs, stream=None) -> None:
     n = int(pairs.shape[0])
     _check(_c["block_copy"](cache.ref, _dev(pairs, "pairs"), n, _stream(stream)), "block_copy")
+
+
+PKV_SWAP_OUT = 0
+PKV_SWAP_IN = 1
+
+
+def block_swap(cache: Cache, host_kv, pairs, to_host: bool, stream=None) -> None:
+    """host_kv: a pinned CPU torch tensor of whole blocks (uint8)."""
+    n = int(pairs.shape[0])
+    nb = host_kv.numel() * host_kv.element_size() // pkv_block_bytes(cache.desc)
+    _check(_c["block_swap"](cache.ref, ctypes.c_void_p(host_kv.data_ptr()), nb,
+                            _dev(pairs, "pairs"), n, PKV_SWAP_OUT if to_host else PKV_SWAP_IN,
+                            _stream(stream)), "block_swap")
 
 
 def pkv_attention_workspace_bytes(cache: Cache, num_q_heads: int, h_seq_lens,

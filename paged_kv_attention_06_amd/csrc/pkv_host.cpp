@@ -355,6 +355,29 @@ int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, 
                     "block_copy");
 }
 
+int block_swap(const pkv_cache* cache, void* host_kv, int64_t num_host_blocks,
+               const int64_t* pairs, int64_t num_pairs, int32_t direction, void* stream) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c)) return e;
+  if (num_pairs < 0 || num_host_blocks < 0)
+    return fail(PKV_ERR_DIM, "num_pairs %lld / num_host_blocks %lld < 0", (long long)num_pairs,
+                (long long)num_host_blocks);
+  if (direction != PKV_SWAP_OUT && direction != PKV_SWAP_IN)
+    return fail(PKV_ERR_RANGE, "direction %d is neither PKV_SWAP_OUT nor PKV_SWAP_IN", direction);
+  if (num_pairs == 0) return ok();
+  if (!host_kv || !pairs) return fail(PKV_ERR_NULL, "host_kv or pairs is NULL");
+  if (num_host_blocks < 1) return fail(PKV_ERR_DIM, "the host pool has no blocks");
+  void* dev = nullptr;
+  if (hipHostGetDevicePointer(&dev, host_kv, 0) != hipSuccess || !dev) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_RANGE, "host_kv is not pinned, device-mapped host memory");
+  }
+  return hip_status(pkv::launch_block_swap(c, static_cast<char*>(dev), pairs, num_pairs,
+                                           direction == PKV_SWAP_OUT,
+                                           static_cast<hipStream_t>(stream)),
+                    "block_swap");
+}
+
 size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads,
                                      const int32_t* h_qsl, const int32_t* h_seq_lens,
                                      int32_t num_seqs) {

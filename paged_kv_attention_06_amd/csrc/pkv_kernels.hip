@@ -255,6 +255,37 @@ hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t n
 }
 
 // ---------------------------------------------------------------------------
+// Block swap: the same granule copy with one side in host memory the GPU
+// reaches through its device mapping (every access crosses the host link;
+// each wave moves 1 KiB per instruction, and many waves keep the link busy).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_block_swap(const char* __restrict__ src_base,
+                                                    char* __restrict__ dst_base,
+                                                    int64_t granules_per_block,
+                                                    const int64_t* __restrict__ pairs,
+                                                    int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t pr = i / granules_per_block;
+  const int64_t g = i % granules_per_block;
+  const uint4* s = reinterpret_cast<const uint4*>(src_base) + pairs[2 * pr] * granules_per_block + g;
+  uint4* d = reinterpret_cast<uint4*>(dst_base) + pairs[2 * pr + 1] * granules_per_block + g;
+  *d = *s;
+}
+
+hipError_t launch_block_swap(const CacheDesc& c, char* host_dev_ptr, const int64_t* pairs,
+                             int64_t num_pairs, bool to_host, hipStream_t stream) {
+  const int64_t gpb = (int64_t)(c.block_bytes / 16);
+  const int64_t total = gpb * num_pairs;
+  if (total == 0) return hipSuccess;
+  const char* src = to_host ? c.kv : host_dev_ptr;
+  char* dst = to_host ? host_dev_ptr : c.kv;
+  hipLaunchKernelGGL(k_block_swap, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     src, dst, gpb, pairs, total);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Decode work units.  A unit is one partition of one decode row: a full
 // 256-token partition, or the shorter last partition of a row.  All full
 // units come first (sequence by sequence), then the partial ones from the

@@ -368,3 +368,42 @@ def test_verify_full_size_sampled_parity():
     got = np.concatenate([out[qsl[s]:qsl[s + 1]] for s in seqs])
     want = np.concatenate([scenario.sequence_attention(w, s) for s in seqs])
     _check_attention(got, want, "bf16", "verify full")
+
+
+# ------------------------------------------------------------------ block swap
+def test_block_swap_out_and_back_in():
+    """Swap the blocks of two sequences out to pinned host memory (they equal
+    the oracle pool's blocks bit for bit), then back in to other device
+    blocks; with the tables rewritten, attention gives the same bits."""
+    from paged_kv_attention_06_amd import _lib as L
+    w = workloads.small(3)
+    _announce("block swap out / in")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    before = st.out.cpu().numpy().copy()
+    seqs = [3, 4]
+    nblk = [-(-int(w.seq_lens[s]) // 16) for s in seqs]
+    blocks = [int(b) for s, n in zip(seqs, nblk) for b in st.tables[s][:n]]
+    bb = st.block_bytes
+    host = torch.zeros(len(blocks) * bb, dtype=torch.uint8, pin_memory=True)
+    out_pairs = torch.tensor([[b, i] for i, b in enumerate(blocks)], dtype=torch.int64).cuda()
+    L.block_swap(st.cache, host, out_pairs, to_host=True)
+    torch.cuda.synchronize()
+    hp = host.numpy().view(np.uint16).reshape(len(blocks), w.num_kv_heads, 2, 16 * w.head_size)
+    assert np.array_equal(hp, ref["pool"][blocks]), "swapped-out blocks"
+    used = {int(b) for s in range(w.batch)
+            for b in st.tables[s][:-(-int(w.seq_lens[s]) // 16)]}
+    fresh = [b for b in range(w.num_blocks) if b not in used][:len(blocks)]
+    in_pairs = torch.tensor([[i, b] for i, b in enumerate(fresh)], dtype=torch.int64).cuda()
+    L.block_swap(st.cache, host, in_pairs, to_host=False)
+    k = 0
+    for s, n in zip(seqs, nblk):
+        st.tables[s][:n] = fresh[k:k + n]
+        k += n
+    st.block_tables = torch.from_numpy(st.tables).cuda()
+    st.out.fill_(0)
+    st.attend()
+    torch.cuda.synchronize()
+    pool = st.pool_codes()
+    assert np.array_equal(pool[fresh], ref["pool"][blocks]), "swapped-in blocks"
+    assert np.array_equal(st.out.cpu().numpy(), before), "attention after swap in"

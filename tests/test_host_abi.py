@@ -225,3 +225,18 @@ def test_argument_checks_return_before_launch():
     assert st == 1
     assert L._c["paged_kv_write"](ctypes.byref(good), None, None, None, 0, None) == 0
     assert L._c["block_copy"](ctypes.byref(good), None, -1, None) == 2
+
+
+def test_block_swap_argument_checks():
+    """Errors come back before anything is launched: bad direction or counts,
+    NULL pointers, and host memory that is not pinned and device-mapped."""
+    d = P.descriptor(16, 8, 128, P.PKV_BF16, kv_ptr=0x1000)
+    host = np.zeros(65536 * 2, np.uint8)
+    hp = host.ctypes.data_as(ctypes.c_void_p)
+    f = L._c["block_swap"]
+    assert f(ctypes.byref(d), hp, 2, 1, 1, 5, None) == 7          # direction
+    assert f(ctypes.byref(d), hp, 2, 1, -1, 0, None) == 2         # negative count
+    assert f(ctypes.byref(d), hp, 2, 1, 0, 0, None) == 0          # nothing to do
+    assert f(ctypes.byref(d), None, 2, 1, 1, 0, None) == 1        # NULL host pool
+    assert f(ctypes.byref(d), hp, 2, None, 1, 1, None) == 1       # NULL pairs
+    assert f(ctypes.byref(d), hp, 2, 1, 1, 0, None) == 7          # malloc'd, not pinned

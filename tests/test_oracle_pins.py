@@ -440,3 +440,19 @@ def test_fp8_kv_write_layout_and_skip():
                 assert pool[blk, hh, 1, d * 16 + off] == vq[t, hh, d]
     touched = 2 * 2 * 2 * 64
     assert int((pool != 0x7F).sum()) <= touched
+
+
+def test_block_swap_round_trip_and_untouched():
+    """Swap out to host blocks, swap back in to other device blocks: the
+    blocks come back bit for bit; nothing else changes."""
+    rng = np.random.default_rng(8)
+    dev = rng.integers(0, 1 << 16, size=(10, 2, 2, 16 * 64), dtype=np.uint16)
+    host = np.zeros((6, 2, 2, 16 * 64), np.uint16)
+    before = dev.copy()
+    po.block_swap(dev, host, [(3, 0), (7, 5), (1, 2)], to_host=True)
+    assert np.array_equal(host[[0, 5, 2]], before[[3, 7, 1]])
+    assert not host[[1, 3, 4]].any() and np.array_equal(dev, before)
+    po.block_swap(dev, host, [(0, 8), (5, 9), (2, 0)], to_host=False)
+    assert np.array_equal(dev[[8, 9, 0]], before[[3, 7, 1]])
+    untouched = [b for b in range(10) if b not in (8, 9, 0)]
+    assert np.array_equal(dev[untouched], before[untouched])
