@@ -260,6 +260,108 @@ class CowPool:
 
 
 # ----------------------------------------------------------------------------
+# prefix caching (Inside vLLM "Prefix caching"; vLLM 技术内幕 section 4):
+# every full block gets a chained hash of its parent's hash and its token
+# ids; a new request walks its full blocks from the first and reuses every
+# cached block until the first miss; blocks registered after their KV are
+# written; released blocks that still carry a hash go to the tail of the free
+# queue (evicted last), others to the head; a hashed block loses its hash when
+# it is taken from the head for a new use.  The hash is 64-bit FNV-1a (a
+# published function) over the parent hash (8 bytes, little-endian) and the
+# block's token ids (4 bytes each, little-endian); a hit also compares the
+# stored parent hash and token ids.
+# ----------------------------------------------------------------------------
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET) -> int:
+    for byte in data:
+        h ^= byte
+        h = (h * FNV64_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def block_hash(parent: int, tokens) -> int:
+    data = int(parent).to_bytes(8, "little") + b"".join(
+        int(t & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
+
+
+def prefix_hashes(tokens, block_size: int = BLOCK_SIZE):
+    """Chained hashes of the full blocks of a token-id list (parent of the
+    first block: 0)."""
+    out, parent = [], 0
+    for i in range(len(tokens) // block_size):
+        parent = block_hash(parent, tokens[i * block_size:(i + 1) * block_size])
+        out.append(parent)
+    return out
+
+
+class PrefixCachePool(CowPool):
+    """CowPool plus the prefix cache.  The free queue is a list (head first)."""
+
+    def __init__(self, num_blocks: int, free_order=None, block_size: int = BLOCK_SIZE):
+        super().__init__(num_blocks, free_order, block_size)
+        self.free = list(self.free)
+        self.key = [None] * num_blocks      # (hash, parent, tokens) of a cached block
+        self.by_hash = {}                   # hash -> block
+
+    def _pop(self) -> int:
+        b = self.free.pop(0)
+        if self.key[b] is not None:         # evicted from the cache on reuse
+            h = self.key[b][0]
+            if self.by_hash.get(h) == b:
+                del self.by_hash[h]
+            self.key[b] = None
+        self.ref[b] = 1
+        return b
+
+    def release(self, table: list) -> None:
+        for b in reversed(table):
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                if self.key[b] is not None:
+                    self.free.append(b)
+                else:
+                    self.free.insert(0, b)
+        table.clear()
+
+    def match_prefix(self, tokens) -> list:
+        """Longest run of cached full blocks from the start; each hit gains a
+        reference (leaving the free queue if it was there)."""
+        bs = self.block_size
+        hits, parent = [], 0
+        for i in range(len(tokens) // bs):
+            blk = [int(t) for t in tokens[i * bs:(i + 1) * bs]]
+            h = block_hash(parent, blk)
+            b = self.by_hash.get(h)
+            if b is None or self.key[b] != (h, parent, tuple(blk)):
+                break
+            if self.ref[b] == 0:
+                self.free.remove(b)
+            self.ref[b] += 1
+            hits.append(b)
+            parent = h
+        return hits
+
+    def cache_blocks(self, tokens, table, num_full: int) -> None:
+        """Register the first num_full blocks of a sequence (their KV is
+        written); a block already cached, or a hash another block holds, is
+        left as it is."""
+        bs = self.block_size
+        parent = 0
+        for i in range(num_full):
+            blk = tuple(int(t) for t in tokens[i * bs:(i + 1) * bs])
+            h = block_hash(parent, blk)
+            b = int(table[i])
+            if self.key[b] is None and h not in self.by_hash:
+                self.key[b] = (h, parent, blk)
+                self.by_hash[h] = b
+            parent = h
+
+
+# ----------------------------------------------------------------------------
 # the two data movements
 # ----------------------------------------------------------------------------
 def kv_write(pool: np.ndarray, dtype: str, k_new: np.ndarray, v_new: np.ndarray,

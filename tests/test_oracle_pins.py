@@ -456,3 +456,78 @@ def test_block_swap_round_trip_and_untouched():
     assert np.array_equal(dev[[8, 9, 0]], before[[3, 7, 1]])
     untouched = [b for b in range(10) if b not in (8, 9, 0)]
     assert np.array_equal(dev[untouched], before[untouched])
+
+
+# ------------------------------------------------------------- prefix caching
+def test_fnv1a64_published_vectors():
+    assert po.fnv1a64(b"") == 0xCBF29CE484222325
+    assert po.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert po.fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_block_hashes_chain_the_prefix():
+    """A block's hash stands for the whole prefix up to it: equal prefixes
+    give equal hashes; one changed token changes its block's hash and every
+    later one; a partly filled last block gets none."""
+    rng = np.random.default_rng(9)
+    a = rng.integers(0, 32000, size=16 * 5 + 7).tolist()
+    b = list(a)
+    b[16 * 2 + 3] += 1
+    ha, hb = po.prefix_hashes(a), po.prefix_hashes(b)
+    assert len(ha) == 5
+    assert ha[:2] == hb[:2]
+    assert all(x != y for x, y in zip(ha[2:], hb[2:]))
+    assert po.prefix_hashes(a[:40]) == ha[:2]
+
+
+def test_prefix_cache_walkthrough():
+    """Inside vLLM "Prefix caching": the first request with a long prefix
+    finds nothing and registers its full blocks; after it finishes they sit
+    in the free queue with their hashes; a second request with the same
+    prefix reuses all of them (taken off the queue); had the first still been
+    alive, the counts would be 2."""
+    pool = po.PrefixCachePool(64)
+    prefix = list(range(1000, 1000 + 16 * 4))              # n = 4 full blocks
+    r1 = prefix + [7, 8, 9]
+    assert pool.match_prefix(r1) == []
+    t1 = []
+    pool.append(t1, 0, len(r1))
+    pool.cache_blocks(r1, t1, len(r1) // 16)
+    shared = t1[:4]
+    pool.release(t1)
+    assert all(pool.ref[b] == 0 for b in shared)
+    assert pool.free[-4:] == shared[::-1]                  # hashed blocks at the tail, the first block last
+    r2 = prefix + [5, 5]
+    hit = pool.match_prefix(r2)
+    assert hit == shared and all(pool.ref[b] == 1 for b in hit)
+    assert not any(b in pool.free for b in hit)
+    hit3 = pool.match_prefix(prefix)                       # a third, concurrent request
+    assert hit3 == shared and all(pool.ref[b] == 2 for b in hit3)
+
+
+def test_prefix_cache_eviction_and_release_order():
+    """A block loses its hash only when it is taken from the head for a new
+    use; released unhashed blocks go to the head, hashed ones to the tail."""
+    pool = po.PrefixCachePool(6)
+    toks = list(range(16 * 2))
+    t = []
+    pool.append(t, 0, 32)
+    pool.cache_blocks(toks, t, 2)
+    t_other = []
+    pool.append(t_other, 0, 16)                            # unhashed
+    pool.release(t)
+    pool.release(t_other)
+    assert pool.free[0] == 2 and pool.free[-2:] == [1, 0]
+    grab = []
+    pool.append(grab, 0, 16 * 4)                           # takes 2, 3, 4, 5
+    assert pool.match_prefix(toks) == [0, 1]               # still cached
+    pool.release([0, 1])
+    pool.release(grab)
+    pool2 = po.PrefixCachePool(3)
+    t2 = []
+    pool2.append(t2, 0, 32)
+    pool2.cache_blocks(toks, t2, 2)
+    pool2.release(t2)                                      # free: 2, 1, 0
+    x = []
+    pool2.append(x, 0, 32)                                 # takes 2 then 1: 1 is evicted
+    assert pool2.key[1] is None and pool2.match_prefix(toks) == [0]
