@@ -242,8 +242,37 @@ int pkv_pool_fork(pkv_pool* pool, const int32_t* table, int32_t num_table_blocks
                   int32_t* out_table);
 
 /* Drop one reference of each listed block, last first; a block whose count
- * reaches 0 goes to the head of the free list (reused first). */
+ * reaches 0 goes to the head of the free list (reused first), or to its tail
+ * if it carries a prefix-cache hash (see pkv_pool_cache_blocks). */
 int pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t num_table_blocks);
+
+/* ------------------------------------------------------ prefix caching */
+/* Prefix caching (Inside vLLM, "Prefix caching"; vLLM 技术内幕 section 4):
+ * every full block of a request's token ids gets a chained hash of its
+ * parent block's hash and its own token ids; a new request reuses cached
+ * blocks from its first block up to the first miss; blocks are registered
+ * once their K/V are written.  Released blocks that still carry a hash go to
+ * the tail of the free queue (evicted last, the request's first block last
+ * of all) and others to its head; a hashed block leaves the cache only when
+ * it is taken from the head for a new use (pkv_pool_append). */
+
+/* Hash of one block: 64-bit FNV-1a over `parent` (8 bytes, little-endian;
+ * 0 for a request's first block) followed by the num_tokens token ids (4
+ * bytes each, little-endian). */
+uint64_t pkv_block_hash(uint64_t parent, const int32_t* tokens, int32_t num_tokens);
+
+/* Longest cached prefix of a request's token ids (host int32 [num_tokens];
+ * full blocks only, at most max_blocks): its block ids go to table[0 ..
+ * *num_hit), each gaining a reference (a free block leaves the free queue).
+ * A hit also compares the cached block's parent hash and token ids. */
+int pkv_pool_match_prefix(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* table, int32_t max_blocks, int32_t* num_hit);
+
+/* Register the first num_full_blocks blocks of a sequence (host table of
+ * held ids) as cached for its token ids.  A block that already carries a
+ * hash, or whose hash another block holds, is left as it is. */
+int pkv_pool_cache_blocks(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                          const int32_t* table, int32_t num_full_blocks);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     paged_kv_write,
     pkv_attention_workspace_bytes,
     pkv_block_bytes,
+    pkv_block_hash,
     pkv_build_slot_mapping,
     status_string,
     version,

@@ -78,6 +78,11 @@ _c["pkv_pool_append"] = _sig("pkv_pool_append", ctypes.c_int,
                              [_vp, _i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _i64p, _i64p])
 _c["pkv_pool_fork"] = _sig("pkv_pool_fork", ctypes.c_int, [_vp, _i32p, ctypes.c_int32, _i32p])
 _c["pkv_pool_release"] = _sig("pkv_pool_release", ctypes.c_int, [_vp, _i32p, ctypes.c_int32])
+_c["pkv_block_hash"] = _sig("pkv_block_hash", ctypes.c_uint64, [ctypes.c_uint64, _i32p, ctypes.c_int32])
+_c["pkv_pool_match_prefix"] = _sig("pkv_pool_match_prefix", ctypes.c_int,
+                                   [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, _i32p])
+_c["pkv_pool_cache_blocks"] = _sig("pkv_pool_cache_blocks", ctypes.c_int,
+                                   [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32])
 
 EXPORTED = tuple(_c)
 
@@ -278,3 +283,22 @@ class Pool:
 
     def release(self, table: np.ndarray, n_blocks: int) -> None:
         _check(_c["pkv_pool_release"](self.h, _ptr_i32(table), n_blocks), "pkv_pool_release")
+
+    def match_prefix(self, tokens, table: np.ndarray) -> int:
+        """Cached full blocks from the start of `tokens` go to table[:n]; returns n."""
+        t = _host_i32(tokens)
+        assert table.dtype == np.int32 and table.flags.c_contiguous
+        n = ctypes.c_int32(0)
+        _check(_c["pkv_pool_match_prefix"](self.h, _ptr_i32(t), t.shape[0], _ptr_i32(table),
+                                           table.shape[0], ctypes.byref(n)), "pkv_pool_match_prefix")
+        return int(n.value)
+
+    def cache_blocks(self, tokens, table: np.ndarray, num_full_blocks: int) -> None:
+        t = _host_i32(tokens)
+        _check(_c["pkv_pool_cache_blocks"](self.h, _ptr_i32(t), t.shape[0], _ptr_i32(table),
+                                           num_full_blocks), "pkv_pool_cache_blocks")
+
+
+def pkv_block_hash(parent: int, tokens) -> int:
+    t = _host_i32(tokens)
+    return int(_c["pkv_block_hash"](parent, _ptr_i32(t), t.shape[0]))

@@ -11,6 +11,7 @@
 #include <deque>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv.h"
@@ -414,10 +415,71 @@ int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q, int
 // ---------------------------------------------------------------------------
 // host block allocator
 // ---------------------------------------------------------------------------
+// The free queue is a doubly linked list over block ids, so a block can leave
+// it from anywhere in O(1) (a prefix-cache hit on a free block).  Blocks that
+// carry a prefix hash keep it (and their place in the cache map) until they
+// are taken from the head for a new use.
 struct pkv_pool {
   int32_t block_size;
   std::vector<int32_t> ref;
-  std::deque<int32_t> free_list;
+  std::vector<int32_t> prev, next;  // free-queue links (-1 = none)
+  std::vector<char> in_free;
+  int32_t head = -1, tail = -1;
+  int64_t nfree = 0;
+  // prefix cache: per block its hash, its parent's hash and its token ids
+  std::vector<char> hashed;
+  std::vector<uint64_t> hash, parent;
+  std::vector<int32_t> toks;  // [num_blocks][block_size], filled on registration
+  std::unordered_map<uint64_t, int32_t> by_hash;
+
+  void push_back(int32_t b) {
+    prev[b] = tail;
+    next[b] = -1;
+    if (tail >= 0) next[tail] = b; else head = b;
+    tail = b;
+    in_free[b] = 1;
+    ++nfree;
+  }
+  void push_front(int32_t b) {
+    next[b] = head;
+    prev[b] = -1;
+    if (head >= 0) prev[head] = b; else tail = b;
+    head = b;
+    in_free[b] = 1;
+    ++nfree;
+  }
+  void unlink(int32_t b) {
+    if (prev[b] >= 0) next[prev[b]] = next[b]; else head = next[b];
+    if (next[b] >= 0) prev[next[b]] = prev[b]; else tail = prev[b];
+    prev[b] = next[b] = -1;
+    in_free[b] = 0;
+    --nfree;
+  }
+  // Takes the head block for a new use; a cached block loses its hash here.
+  int32_t take() {
+    const int32_t b = head;
+    unlink(b);
+    if (!hashed.empty() && hashed[(size_t)b]) {
+      auto it = by_hash.find(hash[(size_t)b]);
+      if (it != by_hash.end() && it->second == b) by_hash.erase(it);
+      hashed[(size_t)b] = 0;
+    }
+    ref[(size_t)b] = 1;
+    return b;
+  }
+  void drop(int32_t b) {  // one reference less; at zero back to the queue
+    if (--ref[(size_t)b] == 0) {
+      if (!hashed.empty() && hashed[(size_t)b]) push_back(b); else push_front(b);
+    }
+  }
+  void ensure_cache() {
+    if (!hashed.empty()) return;
+    const size_t n = ref.size();
+    hashed.assign(n, 0);
+    hash.assign(n, 0);
+    parent.assign(n, 0);
+    toks.assign(n * (size_t)block_size, 0);
+  }
 };
 
 pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t block_size) {
@@ -430,6 +492,9 @@ pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t
   if (!p) return nullptr;
   p->block_size = block_size;
   p->ref.assign((size_t)num_blocks, 0);
+  p->prev.assign((size_t)num_blocks, -1);
+  p->next.assign((size_t)num_blocks, -1);
+  p->in_free.assign((size_t)num_blocks, 0);
   std::vector<char> seen;
   if (free_order) seen.assign((size_t)num_blocks, 0);
   for (int64_t i = 0; i < num_blocks; ++i) {
@@ -443,7 +508,7 @@ pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t
       }
       seen[(size_t)b] = 1;
     }
-    p->free_list.push_back(b);
+    p->push_back(b);
   }
   ok();
   return p;
@@ -451,9 +516,7 @@ pkv_pool* pkv_pool_create(int64_t num_blocks, const int32_t* free_order, int32_t
 
 void pkv_pool_destroy(pkv_pool* pool) { delete pool; }
 
-int64_t pkv_pool_num_free(const pkv_pool* pool) {
-  return pool ? (int64_t)pool->free_list.size() : -1;
-}
+int64_t pkv_pool_num_free(const pkv_pool* pool) { return pool ? pool->nfree : -1; }
 
 int32_t pkv_pool_refcnt(const pkv_pool* pool, int32_t block_id) {
   if (!pool || block_id < 0 || (size_t)block_id >= pool->ref.size()) return -1;
@@ -480,16 +543,11 @@ int pkv_pool_append(pkv_pool* pool, int32_t* table, int32_t max_blocks, int32_t 
   const bool into_partial = n_new > 0 && (cur_len % bs) != 0;
   const bool copy = into_partial && pool->ref[(size_t)table[have - 1]] > 1;
   const int64_t fresh = (need - have) + (copy ? 1 : 0);
-  if (fresh > (int64_t)pool->free_list.size())
-    return fail(PKV_ERR_NOMEM, "pkv_pool_append: %lld blocks needed, %zu free", (long long)fresh,
-                pool->free_list.size());
+  if (fresh > pool->nfree)
+    return fail(PKV_ERR_NOMEM, "pkv_pool_append: %lld blocks needed, %lld free", (long long)fresh,
+                (long long)pool->nfree);
   cow_pair[0] = cow_pair[1] = -1;
-  auto take = [pool]() {
-    const int32_t b = pool->free_list.front();
-    pool->free_list.pop_front();
-    pool->ref[(size_t)b] = 1;
-    return b;
-  };
+  auto take = [pool]() { return pool->take(); };
   if (copy) {
     const int32_t old_b = table[have - 1];
     const int32_t new_b = take();
@@ -527,10 +585,82 @@ int pkv_pool_release(pkv_pool* pool, const int32_t* table, int32_t n) {
     if (table[i] < 0 || (size_t)table[i] >= pool->ref.size() || pool->ref[(size_t)table[i]] < 1)
       return fail(PKV_ERR_RANGE, "pkv_pool_release: entry %d (%d) is not a held block", i, table[i]);
   }
-  for (int32_t i = n - 1; i >= 0; --i) {
-    int32_t& r = pool->ref[(size_t)table[i]];
-    r -= 1;
-    if (r == 0) pool->free_list.push_front(table[i]);
+  for (int32_t i = n - 1; i >= 0; --i) pool->drop(table[i]);
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// prefix caching
+// ---------------------------------------------------------------------------
+uint64_t pkv_block_hash(uint64_t parent, const int32_t* tokens, int32_t num_tokens) {
+  uint64_t h = 0xCBF29CE484222325ull;
+  auto mix = [&h](uint64_t v, int nbytes) {
+    for (int i = 0; i < nbytes; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= 0x100000001B3ull;
+    }
+  };
+  mix(parent, 8);
+  for (int32_t i = 0; i < num_tokens; ++i) mix((uint32_t)tokens[i], 4);
+  return h;
+}
+
+int pkv_pool_match_prefix(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                          int32_t* table, int32_t max_blocks, int32_t* num_hit) {
+  if (!pool || !num_hit || (num_tokens > 0 && !tokens) || (max_blocks > 0 && !table))
+    return fail(PKV_ERR_NULL, "pkv_pool_match_prefix: NULL argument");
+  if (num_tokens < 0 || max_blocks < 0) return fail(PKV_ERR_DIM, "pkv_pool_match_prefix: negative count");
+  *num_hit = 0;
+  if (pool->hashed.empty()) return ok();
+  const int32_t bs = pool->block_size;
+  uint64_t par = 0;
+  int32_t n = 0;
+  for (int32_t i = 0; i < num_tokens / bs && i < max_blocks; ++i) {
+    const int32_t* blk = tokens + (size_t)i * bs;
+    const uint64_t h = pkv_block_hash(par, blk, bs);
+    auto it = pool->by_hash.find(h);
+    if (it == pool->by_hash.end()) break;
+    const int32_t b = it->second;
+    if (pool->parent[(size_t)b] != par ||
+        std::memcmp(&pool->toks[(size_t)b * bs], blk, sizeof(int32_t) * bs) != 0)
+      break;
+    if (pool->ref[(size_t)b] == 0) pool->unlink(b);
+    pool->ref[(size_t)b] += 1;
+    table[n++] = b;
+    par = h;
+  }
+  *num_hit = n;
+  return ok();
+}
+
+int pkv_pool_cache_blocks(pkv_pool* pool, const int32_t* tokens, int32_t num_tokens,
+                          const int32_t* table, int32_t num_full_blocks) {
+  if (!pool || (num_full_blocks > 0 && (!tokens || !table)))
+    return fail(PKV_ERR_NULL, "pkv_pool_cache_blocks: NULL argument");
+  if (num_full_blocks < 0 || num_tokens < 0) return fail(PKV_ERR_DIM, "pkv_pool_cache_blocks: negative count");
+  const int32_t bs = pool->block_size;
+  if ((int64_t)num_full_blocks * bs > num_tokens)
+    return fail(PKV_ERR_RANGE, "pkv_pool_cache_blocks: %d full blocks need %lld tokens, %d given",
+                num_full_blocks, (long long)num_full_blocks * bs, num_tokens);
+  for (int32_t i = 0; i < num_full_blocks; ++i) {
+    if (table[i] < 0 || (size_t)table[i] >= pool->ref.size() || pool->ref[(size_t)table[i]] < 1)
+      return fail(PKV_ERR_RANGE, "pkv_pool_cache_blocks: entry %d (%d) is not a held block", i,
+                  table[i]);
+  }
+  pool->ensure_cache();
+  uint64_t par = 0;
+  for (int32_t i = 0; i < num_full_blocks; ++i) {
+    const int32_t* blk = tokens + (size_t)i * bs;
+    const uint64_t h = pkv_block_hash(par, blk, bs);
+    const size_t b = (size_t)table[i];
+    if (!pool->hashed[b] && pool->by_hash.find(h) == pool->by_hash.end()) {
+      pool->hashed[b] = 1;
+      pool->hash[b] = h;
+      pool->parent[b] = par;
+      std::memcpy(&pool->toks[b * bs], blk, sizeof(int32_t) * bs);
+      pool->by_hash.emplace(h, (int32_t)b);
+    }
+    par = h;
   }
   return ok();
 }

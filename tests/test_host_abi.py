@@ -240,3 +240,54 @@ def test_block_swap_argument_checks():
     assert f(ctypes.byref(d), None, 2, 1, 1, 0, None) == 1        # NULL host pool
     assert f(ctypes.byref(d), hp, 2, None, 1, 1, None) == 1       # NULL pairs
     assert f(ctypes.byref(d), hp, 2, 1, 1, 0, None) == 7          # malloc'd, not pinned
+
+
+def test_block_hash_matches_oracle():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        parent = int(rng.integers(0, 2**63))
+        toks = rng.integers(-2**31, 2**31, size=16).astype(np.int32)
+        assert P.pkv_block_hash(parent, toks) == po.block_hash(parent, toks.tolist())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_prefix_cache_replay_matches_oracle(seed):
+    """Requests from a few shared-prefix families arrive, reuse their cached
+    prefix, append the rest, register their full blocks and finish at random;
+    the library's pool and the oracle's take identical decisions (hits,
+    tables, reference counts, free counts), evictions included."""
+    rng = np.random.default_rng(100 + seed)
+    nb = 160
+    order = rng.permutation(nb).astype(np.int32)
+    lib = P.Pool(nb, order)
+    ora = po.PrefixCachePool(nb, order)
+    families = [rng.integers(0, 50000, size=int(n)).tolist() for n in (40, 96, 130, 16)]
+    live = []
+    total_hits = 0
+    for step in range(300):
+        if live and (rng.random() < 0.45 or lib.num_free() < 40):
+            i = int(rng.integers(len(live)))
+            toks, t_lib, t_ora = live.pop(i)
+            n = -(-len(toks) // 16)
+            lib.release(t_lib, n)
+            ora.release(t_ora)
+        else:
+            fam = families[int(rng.integers(len(families)))]
+            cut = int(rng.integers(len(fam) // 2, len(fam) + 1))
+            toks = fam[:cut] + rng.integers(0, 50000, size=int(rng.integers(1, 40))).tolist()
+            t_lib = np.zeros(32, np.int32)
+            hits = lib.match_prefix(toks, t_lib)
+            hits_o = ora.match_prefix(toks)
+            assert t_lib[:hits].tolist() == hits_o
+            total_hits += hits
+            t_ora = list(hits_o)
+            lib.append(t_lib, hits * 16, len(toks) - hits * 16)
+            ora.append(t_ora, hits * 16, len(toks) - hits * 16)
+            n = -(-len(toks) // 16)
+            assert t_lib[:n].tolist() == t_ora
+            lib.cache_blocks(toks, t_lib, len(toks) // 16)
+            ora.cache_blocks(toks, t_ora, len(toks) // 16)
+            live.append((toks, t_lib, t_ora))
+        assert lib.num_free() == len(ora.free)
+        assert [lib.refcnt(b) for b in range(nb)] == ora.ref
+    assert total_hits > 50
