@@ -383,7 +383,7 @@ def main() -> None:
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": None if verify else (MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
                                             MEASURED_TRAFFIC_BYTES),
-            "kernel": ("paged_attention_mixed (k_v_fp16 + k_prefill_tile)" if verify else
+            "kernel": ("paged_attention_mixed (k_prefill_tile, bf16 V)" if verify else
                        "paged_attention_decode (k_decode_stream, one launch)"),
             "algorithmic_bytes_per_launch": alg,
         },

@@ -89,6 +89,7 @@ struct Plan {
   int64_t class_count[pkv::kPartClasses] = {0};
   int64_t prefill_tiles = 0;
   int prefill_seqs = 0;
+  int64_t max_prefill_q = 0;  // longest q_len of a prefill row
   int64_t prefill_vblocks = 0;
   int64_t num_tokens = 0;
   int64_t stream_steps = 0;  // per kv head: sum over decode rows of steps + setup charge
@@ -125,6 +126,7 @@ int plan_attention(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs
       const int tq = pkv::prefill_tile_q(group);
       plan->prefill_tiles += (ql + tq - 1) / tq;
       plan->prefill_seqs += 1;
+      if (ql > plan->max_prefill_q) plan->max_prefill_q = ql;
       plan->prefill_vblocks += pkv::prefill_vblocks(L);
     }
     plan->num_tokens += ql;
@@ -146,6 +148,18 @@ int64_t stream_wave_cap(const Plan& p, int hkv) {
 unsigned first_epoch() {
   const auto t = std::chrono::steady_clock::now().time_since_epoch().count();
   return (unsigned)t ^ (unsigned)((unsigned long long)t >> 32) ^ 0x9E3779B9u;
+}
+
+// Prefill tiles of calls whose prefill rows are all short (at most 64 query
+// rows: speculative verify, small chunks) read bf16 V straight from the pool,
+// with P as a bf16 hi + lo pair: such calls are bound by HBM, and the fp16
+// copy of V would read V twice and write it once more.  Long chunks keep the
+// fp16 copy (one P.V MFMA per step).  PKV_PREFILL_V=bf16|fp16 forces either.
+bool prefill_reads_bf16_v(const Plan& p) {
+  const char* e = std::getenv("PKV_PREFILL_V");
+  if (e && std::strcmp(e, "bf16") == 0) return true;
+  if (e && std::strcmp(e, "fp16") == 0) return false;
+  return p.max_prefill_q <= 64;
 }
 
 // Decode rows without prefill rows use the stream kernel unless
@@ -241,6 +255,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.class_start[0] = 0;
   for (int k = 0; k < pkv::kPartClasses; ++k) a.class_start[k + 1] = a.class_start[k] + plan.class_count[k];
   a.prefill_tiles = plan.prefill_tiles;
+  a.prefill_v_bf16 = prefill_reads_bf16_v(plan);
   a.prefill_seqs = plan.prefill_seqs;
   a.prefill_vblocks = plan.prefill_vblocks;
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;

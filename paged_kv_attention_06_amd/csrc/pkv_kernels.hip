@@ -1823,7 +1823,10 @@ __global__ __launch_bounds__(256) void k_v_fp16(PrefillParams p) {
 // They must be distinct __shared__ arrays: the compiler then sees that the
 // copies into one stage cannot alias the reads of the other and does not
 // make the reads wait for those copies.
-template <int D, int G>
+// VB: V is read as bf16 straight from the pool (through the block table,
+// like K) and P enters the P.V product as a bf16 hi + lo pair (two MFMAs);
+// otherwise V comes from the fp16 copy k_v_fp16 made in the workspace.
+template <int D, int G, bool VB>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds0,
                                              char* lds1) {
   using S = PrefillShape<D, G>;
@@ -1884,7 +1887,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   const int nkt = (pend + S::KT - 1) / S::KT;      // key tiles needed (keys < pend)
   const int nbl = (L + BS - 1) / BS;               // valid block-table entries
   const char* k_src = p.kv + (size_t)kvh * 2 * S::TILE + lane * 16;
-  const char* v_src = p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
+  const char* v_src = VB ? p.kv + (size_t)(2 * kvh + 1) * S::TILE + lane * 16
+                        : p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
 
   // Per-tile metadata travels in one vector load issued with the copies of
   // the tile before (scalar loads would make every later LDS wait also wait
@@ -1895,8 +1899,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   int meta = 0;
   auto load_meta = [&](int t) {
     const int i = lane & 3;
-    const int32_t* src = lane < 4 ? bt_row + min(t * 4 + i, nbl - 1)
-                                  : exp_row + max(t - 1, 0) * 4 + i;
+    const int32_t* src = (lane < 4 || VB) ? bt_row + min(t * 4 + i, nbl - 1)
+                                          : exp_row + max(t - 1, 0) * 4 + i;
     meta = *src;
   };
 
@@ -1913,11 +1917,30 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 #pragma unroll
       for (int i = 0; i < S::CP; ++i)
         __builtin_amdgcn_global_load_lds(ks + i * 1024, (lds_void_t*)(kd + i * 1024), 16, 0, 0);
-    }
-    const char* vs = v_src + (size_t)blk * p.hkv * S::TILE;
+      if constexpr (VB) {
+        const char* vs = v_src + (size_t)id * p.block_bytes;
 #pragma unroll
-    for (int i = 0; i < S::CP; ++i)
-      __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
+        for (int i = 0; i < S::CP; ++i)
+          __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
+      }
+    }
+    if constexpr (!VB) {
+      const char* vs = v_src + (size_t)blk * p.hkv * S::TILE;
+#pragma unroll
+      for (int i = 0; i < S::CP; ++i)
+        __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
+    }
+  };
+  // VB: keys at or past L in the tile (unwritten slots of the last block,
+  // stale LDS of blocks past the table) get a zero V, so that a zero
+  // probability never meets a NaN.  Wave w clears its block's tail.
+  auto clear_v_tail = [&](int kt, char* stage) {
+    const int kb = kt * S::KT + wave * BS;         // first key of block `wave`
+    const int t0 = max(0, min(BS, L - kb));        // its first invalid token
+    if (t0 == BS) return;
+    uint16_t* vt = reinterpret_cast<uint16_t*>(stage + (4 + wave) * S::TILE);
+    for (int d = lane; d < D; d += 64)
+      for (int t = t0; t < BS; ++t) vt[((t >> 3) * D + d) * 8 + (t & 7)] = 0;
   };
 
   f32x16_t o[S::DB];
@@ -1993,6 +2016,35 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
         for (int i = 0; i < 16; ++i) o[db][i] *= corr;
     }
     const float nm = -m_run;
+    if constexpr (VB) {
+      // P = hi + lo, both bf16 (16 significant bits together); V is bf16
+      uint32_t ph[8], pl[8];
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w], c, nm));
+        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w + 1], c, nm));
+        l_run += a + b;
+        const bf16x2_t hi = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+        const float ah = bf16_lo(__builtin_bit_cast(uint32_t, hi));
+        const float bh = bf16_hi(__builtin_bit_cast(uint32_t, hi));
+        ph[w] = __builtin_bit_cast(uint32_t, hi);
+        pl[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - ah, b - bh}, bf16x2_t));
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8_t bh = __builtin_bit_cast(
+            bf16x8_t, make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]));
+        const bf16x8_t bl = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]));
+#pragma unroll
+        for (int db = 0; db < S::DB; ++db) {
+          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, va[kk][db]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bh, o[db], 0, 0, 0);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bl, o[db], 0, 0, 0);
+        }
+      }
+      return;
+    }
     const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
     uint32_t pk[8];
 #pragma unroll
@@ -2034,6 +2086,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   auto step = [&](int kt, const char* cur, char* nxt) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile kt have landed
     __syncthreads();                       // everyone's have; `nxt` is free again
+    if constexpr (VB) {
+      if (kt * S::KT + S::KT > L) {        // uniform: the tile reaches past the last key
+        clear_v_tail(kt, const_cast<char*>(cur));
+        __syncthreads();
+      }
+    }
     const i32x4_t ex = {__builtin_amdgcn_readlane(meta, 4), __builtin_amdgcn_readlane(meta, 5),
                         __builtin_amdgcn_readlane(meta, 6), __builtin_amdgcn_readlane(meta, 7)};
     if (kt + 1 < nkt) issue(kt + 1, nxt);
@@ -2076,12 +2134,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_tile(
     PrefillParams p) {
   __shared__ __align__(16) char lds0[PrefillLds<D, G>::STAGE];
   __shared__ __align__(16) char lds1[PrefillLds<D, G>::STAGE];
-  prefill_item<D, G>(p, blockIdx.x, lds0, lds1);
+  prefill_item<D, G, VB>(p, blockIdx.x, lds0, lds1);
 }
 
 // One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
@@ -2102,7 +2160,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __align__(16) char lds0[PRE];
   __shared__ __align__(16) char lds1[PRE];
   if ((int)blockIdx.x < m.n_prefill) {
-    prefill_item<D, G>(m.pp, blockIdx.x, lds0, lds1);
+    prefill_item<D, G, false>(m.pp, blockIdx.x, lds0, lds1);
   } else {
     const int wave = threadIdx.x >> 6;
     const int item = ((int)blockIdx.x - m.n_prefill) * 4 + wave;
@@ -2117,13 +2175,16 @@ static hipError_t v_fp16(const PrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool VB>
 static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
-  if (hipError_t e = v_fp16<D>(p, stream)) return e;
+  if constexpr (!VB) {
+    if (hipError_t e = v_fp16<D>(p, stream)) return e;
+  }
+  const dim3 g((unsigned)grid), b(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_prefill_tile<D, 4>), dim3((unsigned)grid), dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1, VB>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2, VB>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill_tile<D, 4, VB>), g, b, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2154,8 +2215,13 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
   const PrefillParams p = make_prefill_params(c, a);
   const int G = a.hq / c.hkv;
   const int64_t grid = a.prefill_tiles * c.hkv;
-  if (c.head_size == 128) return prefill_g<128>(G, p, grid, stream);
-  if (c.head_size == 64) return prefill_g<64>(G, p, grid, stream);
+  if (a.prefill_v_bf16) {
+    if (c.head_size == 128) return prefill_g<128, true>(G, p, grid, stream);
+    if (c.head_size == 64) return prefill_g<64, true>(G, p, grid, stream);
+  } else {
+    if (c.head_size == 128) return prefill_g<128, false>(G, p, grid, stream);
+    if (c.head_size == 64) return prefill_g<64, false>(G, p, grid, stream);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -407,3 +407,23 @@ def test_block_swap_out_and_back_in():
     pool = st.pool_codes()
     assert np.array_equal(pool[fresh], ref["pool"][blocks]), "swapped-in blocks"
     assert np.array_equal(st.out.cpu().numpy(), before), "attention after swap in"
+
+
+@pytest.mark.parametrize("vpath", ["bf16", "fp16"])
+@pytest.mark.parametrize("case", ["verify", "chunk"])
+def test_prefill_v_paths(case, vpath, monkeypatch):
+    """Pure prefill calls read V either as bf16 straight from the pool (P as
+    a bf16 hi + lo pair; keys past L zeroed in LDS) or from the fp16 copy;
+    both against the oracle, on a verify batch and on a 150-row chunk that
+    starts mid-block and ends in a partly filled block."""
+    monkeypatch.setenv("PKV_PREFILL_V", vpath)
+    if case == "verify":
+        w = workloads.make_verify(small_size=True)
+    else:
+        streams = [np.random.default_rng(x) for x in (61, 62, 63, 64)]
+        w = workloads._build(4, "chunk alone", "bf16", 32, 8, 128, 128 ** -0.5,
+                             np.array([37], np.int32), np.array([150], np.int32), 40, streams)
+    _announce(f"prefill V path {vpath}, {case}: L={w.seq_lens.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"{case} via {vpath} V")
