@@ -37,6 +37,11 @@ MEASURED_TRAFFIC_BYTES = 1_351_737_000
 MEASURED_TRAFFIC_BYTES_FP8 = 692_397_000
 
 
+def algorithmic_kv_bytes(w) -> int:
+    """K and V of every valid token of every kv head, once per sequence."""
+    return int(w.seq_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * w.kv_dtype_bytes
+
+
 def algorithmic_bytes(w) -> int:
     """Bytes the decode step must move: K and V of every valid token of every
     kv head (at the cache's element size), the query rows read, the fp32
@@ -48,6 +53,19 @@ def algorithmic_bytes(w) -> int:
     tables = int(((L + 15) // 16).sum()) * 4
     qsl = 4 * (w.batch + 1) if w.num_tokens != w.batch else 0
     return kv + q + out + tables + 4 * w.batch + qsl
+
+
+def unique_kv_bytes(w, tables) -> int:
+    """K/V bytes of the distinct physical blocks the batch reads (a block
+    shared by several sequences counted once, with the most tokens any of
+    them reads from it)."""
+    used = {}
+    for s in range(w.batch):
+        L = int(w.seq_lens[s])
+        for j in range(-(-L // 16)):
+            b = int(tables[s][j])
+            used[b] = max(used.get(b, 0), min(16, L - 16 * j))
+    return sum(used.values()) * 2 * w.num_kv_heads * w.head_size * w.kv_dtype_bytes
 
 
 def cpu_baseline(w, min_s: float = 10.0):
@@ -267,7 +285,7 @@ def main() -> None:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify", "swap",
-                                           "prefix-cache"],
+                                           "prefix-cache", "decode-7b", "decode-13b"],
                     default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
                          "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
@@ -305,7 +323,13 @@ def main() -> None:
 
     fp8 = args.workload == "decode-fp8"
     verify = args.workload == "verify"
-    w = workloads.make_fp8(3) if fp8 else (workloads.make_verify() if verify else workloads.make(3))
+    other = {"decode-7b": 2, "decode-13b": 5}.get(args.workload)
+    if fp8:
+        w = workloads.make_fp8(3)
+    elif verify:
+        w = workloads.make_verify()
+    else:
+        w = workloads.make(other or 3)
     st = gpu_step.PagedStep(w, "cuda")
     st.build_history()
     st.prepare_step()
@@ -342,7 +366,10 @@ def main() -> None:
     value = w.num_tokens / (ms_per_step * 1e-3)
 
     rec = {
-        "metric": (METRIC if not (fp8 or verify) else
+        "metric": (METRIC if not (fp8 or verify or other) else
+                   {2: "decode attention tokens/s & achieved HBM GB/s (% of peak), 7B-MHA batch 64",
+                    5: "decode attention tokens/s & achieved HBM GB/s (% of peak), 13B-MHA batch "
+                       "32, shared prefix + long context"}[other] if other else
                    "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256, "
                    + ("FP8 KV cache" if fp8 else "speculative verify, 4 query rows per sequence")),
         "value": value,
@@ -357,9 +384,16 @@ def main() -> None:
         "dtype": "fp8-e4m3 cache, bf16 q, f32 accumulate" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "Llama-3-8B-shaped GQA decode: 32 q / 8 kv heads, head 128, bf16 "
+            "workload": ({2: "Llama-7B-shaped MHA decode: 32 q / 32 kv heads, head 128, bf16 "
+                             "N(0,1), batch 64, contexts U[128, 2048], pool 1.25x the blocks "
+                             "needed, shuffled",
+                          5: "13B-shaped MHA decode: 40 / 40 heads, head 128, bf16 N(0,1), "
+                             "16 forks of a 1032-token prompt (copy-on-write of the shared "
+                             "partial block in the step) + 16 sequences U[1, 16384] incl. "
+                             "one at 16384"}[other] if other else
+                        "Llama-3-8B-shaped GQA decode: 32 q / 8 kv heads, head 128, bf16 "
                         "N(0,1), batch 256, lognormal contexts (median 800, sigma 1, "
-                        "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool"
+                        "clipped 16..8192), 16-token blocks scattered in a 200,000-block pool")
                         + (", KV cache FP8 E4M3 with K/V scales 1/64" if fp8 else "")
                         + (", each sequence appends and queries its last token plus 3 draft "
                            "tokens (causal)" if verify else ""),
@@ -373,6 +407,9 @@ def main() -> None:
         "write_ms": float((step_ms - attn_ms).mean()),
         "hbm_gbps": achieved,
         "pct_hbm_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "unique_kv_bytes": unique_kv_bytes(w, st.tables),
+        "hbm_gbps_unique_blocks": (alg - algorithmic_kv_bytes(w) + unique_kv_bytes(w, st.tables))
+        / (attn_mean * 1e-3) / 1e9,
         "device_copy_gbps": copy_bandwidth(),
         "wall_s_timed_region": wall,
         "roofline": {
@@ -381,13 +418,13 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if verify else (MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
-                                            MEASURED_TRAFFIC_BYTES),
+            "traffic": None if (verify or other) else (MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
+                                                       MEASURED_TRAFFIC_BYTES),
             "kernel": ("paged_attention_mixed (k_prefill_tile, bf16 V)" if verify else
                        "paged_attention_decode (k_decode_stream, one launch)"),
             "algorithmic_bytes_per_launch": alg,
         },
-        "cpu_baseline": None if (args.no_cpu_baseline or fp8 or verify) else cpu_baseline(w),
+        "cpu_baseline": None if (args.no_cpu_baseline or fp8 or verify or other) else cpu_baseline(w),
     }
     print(json.dumps(rec), flush=True)
 
