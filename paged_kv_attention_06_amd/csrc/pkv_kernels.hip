@@ -1679,14 +1679,10 @@ struct PrefillShape {
   static constexpr int KS = D / 16;             // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;             // 32-row d blocks of O^T
   static constexpr int TILE = BS * D * 2;       // bytes of one block's K (or fp16 V) tile
-  static constexpr int STAGE = 8 * TILE;        // 4 K tiles then 4 V tiles
+  static constexpr int BUF = 4 * TILE;          // one tile's K (or V): 4 blocks
   static constexpr int CP = TILE / 1024;        // 1 KiB copies per tile and wave
 };
 
-template <int D, int G>
-struct PrefillLds {
-  static constexpr int STAGE = PrefillShape<D, G>::STAGE;  // bytes of each of the two stages
-};
 
 // Find (sequence, item, items of that sequence) of work item u, where
 // count(s) gives the items of sequence s.  Every lane gets the result.
@@ -1818,19 +1814,21 @@ __global__ __launch_bounds__(256) void k_v_fp16(PrefillParams p) {
   if (lane == 0) p.vexp[(size_t)kvh * p.vblocks + vb] = e;
 }
 
-// One prefill work item (q tile, kv head) on a whole 4-wave workgroup;
-// `lds0` and `lds1` are the two stages (4 K tiles + 4 fp16 V tiles each).
-// They must be distinct __shared__ arrays: the compiler then sees that the
-// copies into one stage cannot alias the reads of the other and does not
-// make the reads wait for those copies.
+// One prefill work item (q tile, kv head) on a whole 4-wave workgroup.
+// `kb0`, `kb1` (K) and `vb0`, `vb1` (V) are double buffers of one 64-key
+// tile each (4 blocks).  They must be distinct __shared__ arrays: the
+// compiler then sees that the copies into one buffer cannot alias the reads
+// of another and does not make the reads wait for those copies.
 // VB: V is read as bf16 straight from the pool (through the block table,
 // like K) and P enters the P.V product as a bf16 hi + lo pair (two MFMAs);
 // otherwise V comes from the fp16 copy k_v_fp16 made in the workspace.
 template <int D, int G, bool VB>
-__device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* lds0,
-                                             char* lds1) {
+__device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* kb0,
+                                             char* kb1, char* vb0, char* vb1) {
   using S = PrefillShape<D, G>;
   static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
+  constexpr int KS = S::KS, DB = S::DB;
+  constexpr int PVN = (VB ? 4 : 2) * DB;  // P.V products per 32-key chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1839,7 +1837,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   const int item = work / p.hkv;
   int s, tile, ntiles;
   const int32_t* qsl = p.qsl;
-  auto tiles_of = [qsl](int q) {
+  auto tiles_of = [qsl](int q) __attribute__((always_inline)) {
     const int ql = qsl[q + 1] - qsl[q];
     return ql > 1 ? (ql + S::TQ - 1) / S::TQ : 0;
   };
@@ -1884,237 +1882,341 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
     }
   }
 
-  const int nkt = (pend + S::KT - 1) / S::KT;      // key tiles needed (keys < pend)
-  const int nbl = (L + BS - 1) / BS;               // valid block-table entries
+  const int nkt = uniform((pend + S::KT - 1) / S::KT);  // key tiles needed (keys < pend)
+  const int nbl = uniform((L + BS - 1) / BS);           // valid block-table entries
+  // 32-key chunks this wave needs (keys up to its last row's position)
+  const int nch = uniform(wlast >= wp0 ? wlast / 32 + 1 : 0);
   const char* k_src = p.kv + (size_t)kvh * 2 * S::TILE + lane * 16;
   const char* v_src = VB ? p.kv + (size_t)(2 * kvh + 1) * S::TILE + lane * 16
                         : p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
 
   // Per-tile metadata travels in one vector load issued with the copies of
-  // the tile before (scalar loads would make every later LDS wait also wait
-  // for them): lanes 0..3 get the block ids of tile t, lanes 4..7 the V
-  // exponents of tile t - 1.
+  // the iteration before (scalar loads would make every later LDS wait also
+  // wait for them).  Iteration t reads lanes 0..3: block ids of tile t + 2
+  // (its K copies start in iteration t); lanes 4..7: VB, the ids of tile
+  // t + 1 (its V copies start in iteration t), else the V exponents of tile t.
   const int32_t* bt_row = p.block_tables + (size_t)s * p.max_blocks;
   const int32_t* exp_row = p.vexp + (size_t)kvh * p.vblocks + vbase;
-  int meta = 0;
-  auto load_meta = [&](int t) {
+  int meta = bt_row[min(lane & 7, nbl - 1)];  // before the loop: ids of tiles 0 and 1
+  auto load_meta = [&](int t) __attribute__((always_inline)) {
     const int i = lane & 3;
-    const int32_t* src = (lane < 4 || VB) ? bt_row + min(t * 4 + i, nbl - 1)
-                                          : exp_row + max(t - 1, 0) * 4 + i;
+    const int32_t* src = lane < 4 ? bt_row + min((t + 2) * 4 + i, nbl - 1)
+                         : VB     ? bt_row + min((t + 1) * 4 + i, nbl - 1)
+                                  : exp_row + min(t, nkt - 1) * 4 + i;
     meta = *src;
   };
 
-  // ---- wave w copies block w of tile kt (ids in `meta`): its K tile from
-  // the pool (blocks past the table are left stale: their keys are masked)
-  // and its fp16 V tile from the workspace (zero there past L).
-  auto issue = [&](int kt, char* stage) {
-    char* kd = stage + wave * S::TILE;
-    char* vd = kd + 4 * S::TILE;
-    const int blk = kt * 4 + wave;
-    if (blk < nbl) {
-      const int id = __builtin_amdgcn_readlane(meta, wave);
-      const char* ks = k_src + (size_t)id * p.block_bytes;
+  // ---- wave w copies block w of a tile straight into LDS (1 KiB per
+  // instruction): K from the pool (blocks past the table are left stale:
+  // their keys are masked), V from the pool (VB) or from the fp16 copy in
+  // the workspace (zero there past L).  `lane0` is the meta lane of block 0.
+  auto copy_tile = [&](const char* src, char* dst) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < S::CP; ++i)
-        __builtin_amdgcn_global_load_lds(ks + i * 1024, (lds_void_t*)(kd + i * 1024), 16, 0, 0);
-      if constexpr (VB) {
-        const char* vs = v_src + (size_t)id * p.block_bytes;
-#pragma unroll
-        for (int i = 0; i < S::CP; ++i)
-          __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
-      }
+    for (int i = 0; i < S::CP; ++i)
+      __builtin_amdgcn_global_load_lds(src + i * 1024, (lds_void_t*)(dst + i * 1024), 16, 0, 0);
+  };
+  auto issue_k = [&](int kt, char* buf, int lane0) __attribute__((always_inline)) {
+    if (kt * 4 + wave < nbl) {
+      const int id = __builtin_amdgcn_readlane(meta, lane0 + wave);
+      copy_tile(k_src + (size_t)id * p.block_bytes, buf + wave * S::TILE);
     }
-    if constexpr (!VB) {
-      const char* vs = v_src + (size_t)blk * p.hkv * S::TILE;
-#pragma unroll
-      for (int i = 0; i < S::CP; ++i)
-        __builtin_amdgcn_global_load_lds(vs + i * 1024, (lds_void_t*)(vd + i * 1024), 16, 0, 0);
+  };
+  auto issue_v = [&](int kt, char* buf, int lane0) __attribute__((always_inline)) {
+    const int blk = kt * 4 + wave;
+    if constexpr (VB) {
+      if (blk < nbl) {
+        const int id = __builtin_amdgcn_readlane(meta, lane0 + wave);
+        copy_tile(v_src + (size_t)id * p.block_bytes, buf + wave * S::TILE);
+      }
+    } else {
+      copy_tile(v_src + (size_t)blk * p.hkv * S::TILE, buf + wave * S::TILE);
     }
   };
   // VB: keys at or past L in the tile (unwritten slots of the last block,
   // stale LDS of blocks past the table) get a zero V, so that a zero
   // probability never meets a NaN.  Wave w clears its block's tail.
-  auto clear_v_tail = [&](int kt, char* stage) {
+  auto clear_v_tail = [&](int kt, char* vbuf) __attribute__((always_inline)) {
     const int kb = kt * S::KT + wave * BS;         // first key of block `wave`
     const int t0 = max(0, min(BS, L - kb));        // its first invalid token
     if (t0 == BS) return;
-    uint16_t* vt = reinterpret_cast<uint16_t*>(stage + (4 + wave) * S::TILE);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(vbuf + wave * S::TILE);
     for (int d = lane; d < D; d += 64)
       for (int t = t0; t < BS; ++t) vt[((t >> 3) * D + d) * 8 + (t & 7)] = 0;
   };
 
-  f32x16_t o[S::DB];
+  f32x16_t o[DB];
 #pragma unroll
-  for (int db = 0; db < S::DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   // A finite floor keeps exp2(x - m) at 0 for masked x before any key is seen.
   float m_run = -1e30f;
   float l_run = 0.f;
-  int kexp = 0;  // o counts in units of 2^kexp
+  int kexp = 0;        // o counts in units of 2^kexp
+  float corr = 1.f;    // rescale of o that the last softmax asked for
+  bool resc = false;   // (deferred until the P.V products before it are issued)
+  f32x16_t sc[2];      // S^T of the chunks of either parity
+  uint32_t ph[2][8];   // their P: fp16 pairs (VB: the bf16 hi parts)
+  uint32_t pl[2][8];   // VB: the bf16 lo parts
 
-  // ---- one 32-key chunk: scores S^T (MFMA), online softmax, P in fp16,
-  // O^T += V^T P^T (MFMA).  Lane (h, r) of the K operand reads key pi(r).
+  // ---- building blocks of a 32-key chunk.  K operand: lane (h, r) reads key
+  // pi(r) of the chunk; the 16 S^T values a lane then holds are keys
+  // 16 (i / 8) + 8 h + i % 8 of the chunk, the k order of the P.V operands.
   const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-  auto scores = [&](const char* st, int j, f32x16_t& sacc) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    // block 2j + (r >= 16), token pi(r) % 16, d-granule 2 ks + h
-    const char* kp = st + (2 * j + (r >> 4)) * S::TILE + (h * 16 + (pr & 15)) * 16;
-    // all fragments first (the scheduler would otherwise pair each read
-    // with its MFMA and expose the LDS latency eight times)
-    uint4 a[S::KS];
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) a[ks] = *reinterpret_cast<const uint4*>(kp + ks * 512);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks)
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[ks]), qb[ks], sacc,
-                                                     0, 0, 0);
+  auto k_frag = [&](const char* kbuf, int j, int ks) __attribute__((always_inline)) {
+    const char* kp = kbuf + (2 * j + (r >> 4)) * S::TILE + (h * 16 + (pr & 15)) * 16;
+    return *reinterpret_cast<const uint4*>(kp + ks * 512);
   };
-  // Lane (h, r) holds S^T for keys kj + 16 (i / 8) + 8 h + (i % 8), i < 16.
-  auto softmax_pv = [&](const char* st, i32x4_t ex, int k0, int j, f32x16_t& sacc) {
-    const int kj = k0 + 32 * j;
-    // V^T fragments of both 16-key blocks, read before the softmax so their
-    // LDS latency is hidden behind it: block 2j + kk, granule (key group h,
-    // d = 32 db + r)
-    f16x8_t va[2][S::DB];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const char* vp = st + (4 + 2 * j + kk) * S::TILE + (h * D + r) * 16;
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-        va[kk][db] = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(vp + db * 512));
+  // V^T fragment i = kk * DB + db: block 2 j + kk, granule (key group h, d = 32 db + r)
+  auto v_frag = [&](const char* vbuf, int j, int i) __attribute__((always_inline)) {
+    const char* vp = vbuf + (2 * j + i / DB) * S::TILE + (h * D + r) * 16;
+    return *reinterpret_cast<const uint4*>(vp + (i % DB) * 512);
+  };
+  auto qk_mfma = [&](uint4 a, int ks, f32x16_t& s) __attribute__((always_inline)) {
+    const f32x16_t zero = {};
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), qb[ks],
+                                                ks == 0 ? zero : s, 0, 0, 0);
+  };
+  // P.V product i of a chunk: VB, i < 2 DB the hi and then the lo parts of P.
+  auto pv_mfma = [&](uint4 v, int i, const uint32_t (&hi)[8], const uint32_t (&lo)[8]) __attribute__((always_inline)) {
+    const int kk = (i / DB) & 1, db = i % DB;
+    if constexpr (VB) {
+      const uint32_t* w = i < 2 * DB ? hi : lo;
+      const bf16x8_t pb = __builtin_bit_cast(
+          bf16x8_t, make_uint4(w[4 * kk], w[4 * kk + 1], w[4 * kk + 2], w[4 * kk + 3]));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, v), pb, o[db], 0,
+                                                      0, 0);
+    } else {
+      const f16x8_t pb = __builtin_bit_cast(
+          f16x8_t, make_uint4(hi[4 * kk], hi[4 * kk + 1], hi[4 * kk + 2], hi[4 * kk + 3]));
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, v), pb, o[db], 0, 0,
+                                                     0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (__builtin_expect(kj + 31 > wp0, 0)) {  // wave-uniform: the chunk reaches the diagonal
-      const int kl = lim - (kj + 8 * h);  // offsets i' = 16 (i / 8) + i % 8 up to kl are visible
+  };
+  // Softmax of a chunk in pieces: causal mask (chunks that reach the
+  // diagonal), the chunk's row max, the running statistics, then P word w
+  // (keys 2w, 2w + 1 of the lane's 16).
+  auto sm_mask = [&](int ch, f32x16_t& s) __attribute__((always_inline)) {
+    const int kl = lim - (32 * ch + 8 * h);  // offsets 16 (i / 8) + i % 8 up to kl are visible
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = (16 * (i >> 3) + (i & 7) <= kl) ? sacc[i] : -INFINITY;
-    }
-    float mt = __builtin_elementwise_maximum(
-        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[0], sacc[1]),
-                                      __builtin_elementwise_maximum(sacc[2], sacc[3])),
-        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[4], sacc[5]),
-                                      __builtin_elementwise_maximum(sacc[6], sacc[7])));
-    mt = __builtin_elementwise_maximum(
-        mt, __builtin_elementwise_maximum(
-                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[8], sacc[9]),
-                                              __builtin_elementwise_maximum(sacc[10], sacc[11])),
-                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sacc[12], sacc[13]),
-                                              __builtin_elementwise_maximum(sacc[14], sacc[15]))));
+    for (int i = 0; i < 16; ++i) s[i] = (16 * (i >> 3) + (i & 7) <= kl) ? s[i] : -INFINITY;
+  };
+  auto sm_max = [&](const f32x16_t& s) __attribute__((always_inline)) {
+    float a = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[0], s[1]),
+                                            __builtin_elementwise_maximum(s[2], s[3]));
+    float b = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[4], s[5]),
+                                            __builtin_elementwise_maximum(s[6], s[7]));
+    float d = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[8], s[9]),
+                                            __builtin_elementwise_maximum(s[10], s[11]));
+    float e = __builtin_elementwise_maximum(__builtin_elementwise_maximum(s[12], s[13]),
+                                            __builtin_elementwise_maximum(s[14], s[15]));
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b),
+                                         __builtin_elementwise_maximum(d, e));
+  };
+  // New running max only where it grew by more than the slack; the rescale
+  // of o it implies waits for the next slot (P.V of the chunk before is in
+  // flight), l is rescaled here.  Returns -m_run.
+  auto sm_stats = [&](float mt) __attribute__((always_inline)) {
     mt = half_swap_max(mt) * c;
     const bool need = mt > m_run + kRescaleSlack;
-    if (__ballot(need)) {
-      const float mnew = need ? mt : m_run;
-      const float corr = __builtin_amdgcn_exp2f(m_run - mnew);
-      m_run = mnew;
-      l_run *= corr;
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= corr;
-    }
-    const float nm = -m_run;
+    resc = __ballot(need) != 0;
+    const float mnew = need ? mt : m_run;
+    corr = __builtin_amdgcn_exp2f(m_run - mnew);
+    l_run *= corr;
+    m_run = mnew;
+    return -m_run;
+  };
+  auto sm_word = [&](const f32x16_t& s, int w, float nm, uint32_t (&hi)[8], uint32_t (&lo)[8]) __attribute__((always_inline)) {
+    const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w], c, nm));
+    const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * w + 1], c, nm));
     if constexpr (VB) {
       // P = hi + lo, both bf16 (16 significant bits together); V is bf16
-      uint32_t ph[8], pl[8];
+      l_run += a + b;
+      const bf16x2_t ab = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
+      const uint32_t hw = __builtin_bit_cast(uint32_t, ab);
+      hi[w] = hw;
+      lo[w] = __builtin_bit_cast(
+          uint32_t, __builtin_convertvector((f32x2_t){a - bf16_lo(hw), b - bf16_hi(hw)}, bf16x2_t));
+    } else {
+      // P in fp16; l sums the same rounded values that enter the product
+      const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
+      hi[w] = pack_f16x2(a, b);
+      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hi[w]), one, l_run, false);
+    }
+  };
+  auto rescale_o = [&](float f) __attribute__((always_inline)) {
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w], c, nm));
-        const float b = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w + 1], c, nm));
-        l_run += a + b;
-        const bf16x2_t hi = __builtin_convertvector((f32x2_t){a, b}, bf16x2_t);
-        const float ah = bf16_lo(__builtin_bit_cast(uint32_t, hi));
-        const float bh = bf16_hi(__builtin_bit_cast(uint32_t, hi));
-        ph[w] = __builtin_bit_cast(uint32_t, hi);
-        pl[w] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a - ah, b - bh}, bf16x2_t));
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] *= f;
+  };
+
+  // ---- slot ch of the pipeline: S^T of chunk ch + 1 (MFMA), the softmax of
+  // chunk ch (VALU) and O^T += V^T P^T of chunk ch - 1 (MFMA).  The three are
+  // independent, so the softmax runs while the matrix core works.  The K of
+  // chunk ch + 1 and the V of chunk ch - 1 are chunk j of `kbuf` and `vbuf`.
+  constexpr int R = PVN / KS;  // P.V products per QK product in the interleave
+  static_assert(R * KS == PVN, "interleave shape");
+  auto slot_fast = [&](int ch, const char* kbuf, const char* vbuf, int j, const f32x16_t& s_in,
+                       f32x16_t& s_out, const uint32_t (&hin)[8], const uint32_t (&lin)[8],
+                       uint32_t (&hout)[8], uint32_t (&lout)[8]) __attribute__((always_inline)) {
+    // fragments in the order the products consume them, LA groups ahead
+    constexpr int LA = 2;
+    uint4 a[KS], v[2 * DB];
+    auto read_group = [&](int g) __attribute__((always_inline)) {
+      a[g] = k_frag(kbuf, j, g);
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+        if (g * R + u < 2 * DB) v[g * R + u] = v_frag(vbuf, j, g * R + u);
+    };
+#pragma unroll
+    for (int g = 0; g < LA; ++g) read_group(g);
+    __builtin_amdgcn_sched_barrier(0);
+    float mt = 0.f, nm = 0.f;
+#pragma unroll
+    for (int g = 0; g < KS; ++g) {
+      if (g + LA < KS) read_group(g + LA);
+      qk_mfma(a[g], g, s_out);
+#pragma unroll
+      for (int u = 0; u < R; ++u) pv_mfma(v[(g * R + u) % (2 * DB)], g * R + u, hin, lin);
+      if (g == 0) mt = sm_max(s_in);
+      if (g == 1) nm = sm_stats(mt);
+      if (g >= 2) {
+#pragma unroll
+        for (int w = (g - 2) * 8 / (KS - 2); w < (g - 1) * 8 / (KS - 2); ++w)
+          sm_word(s_in, w, nm, hout, lout);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Slots at the ends of a wave's chunks and chunks on the diagonal: the
+  // same work in sequence, each part only where it applies.
+  auto slot_gen = [&](int ch, const char* kbuf, const char* vbuf, int j, f32x16_t& s_in,
+                      f32x16_t& s_out, const uint32_t (&hin)[8], const uint32_t (&lin)[8],
+                      uint32_t (&hout)[8], uint32_t (&lout)[8]) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch >= 1 && ch <= nch) {  // P.V of chunk ch - 1
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t bh = __builtin_bit_cast(
-            bf16x8_t, make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]));
-        const bf16x8_t bl = __builtin_bit_cast(
-            bf16x8_t, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]));
+        uint4 v[DB];
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, va[kk][db]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bh, o[db], 0, 0, 0);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bl, o[db], 0, 0, 0);
+        for (int db = 0; db < DB; ++db) v[db] = v_frag(vbuf, j, kk * DB + db);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          pv_mfma(v[db], kk * DB + db, hin, lin);
+          if constexpr (VB) pv_mfma(v[db], 2 * DB + kk * DB + db, hin, lin);
         }
       }
-      return;
     }
-    const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
-    uint32_t pk[8];
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch + 1 < nch) {  // S^T of chunk ch + 1
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      pk[w] = pack_f16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w], c, nm)),
-                         __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w + 1], c, nm)));
-      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[w]), one, l_run, false);
+      for (int ks = 0; ks < KS; ++ks) qk_mfma(k_frag(kbuf, j, ks), ks, s_out);
     }
-    const int ekk[2] = {j ? ex.z : ex.x, j ? ex.w : ex.y};
+    __builtin_amdgcn_sched_barrier(0);
+    if (ch < nch) {  // softmax of chunk ch
+      if (uniform(32 * ch + 31 > wp0)) sm_mask(ch, s_in);
+      const float nm = sm_stats(sm_max(s_in));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int e = ekk[kk];
-      if (__builtin_expect(e != kexp, 0)) {  // uniform; only with some |v| >= 2^16
-        if (e > kexp) {
-          const float corr = __builtin_ldexpf(1.f, kexp - e);
+      for (int w = 0; w < 8; ++w) sm_word(s_in, w, nm, hout, lout);
+    }
+  };
+  // Before the P.V products of chunk ch - 1: the rescale of o the last
+  // softmax asked for, and (fp16 V copies) the power-of-two exponents e0, e1
+  // of its two blocks.  With E the largest of kexp, e0, e1, o moves to units
+  // of 2^E and block k's probabilities are scaled by 2^(ek - E), so that both
+  // blocks' products land in o's units.  Only tiles with some |v| >= 2^16
+  // have an exponent other than 0.
+  auto pre_slot = [&](int ch, int e0, int e1, uint32_t (&hin)[8]) __attribute__((always_inline)) {
+    if (uniform(resc)) {
+      rescale_o(corr);
+      resc = false;
+    }
+    if constexpr (!VB) {
+      if (uniform(ch >= 1 && ch <= nch && (e0 != kexp || e1 != kexp))) {
+        const int E = max(kexp, max(e0, e1));
+        if (E > kexp) rescale_o(__builtin_ldexpf(1.f, kexp - E));
+        const int ek[2] = {e0, e1};
 #pragma unroll
-          for (int db = 0; db < S::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[db][i] *= corr;
-          kexp = e;
-        } else {
-          const _Float16 f = (_Float16)__builtin_ldexpf(1.f, e - kexp);
+        for (int kk = 0; kk < 2; ++kk) {
+          const _Float16 f = (_Float16)__builtin_ldexpf(1.f, ek[kk] - E);
           const f16x2_t f2 = {f, f};
 #pragma unroll
           for (int w = 4 * kk; w < 4 * kk + 4; ++w)
-            pk[w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, pk[w]) * f2);
+            hin[w] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, hin[w]) * f2);
         }
+        kexp = uniform(E);
       }
-      const f16x8_t bop = __builtin_bit_cast(
-          f16x8_t, make_uint4(pk[4 * kk], pk[4 * kk + 1], pk[4 * kk + 2], pk[4 * kk + 3]));
-#pragma unroll
-      for (int db = 0; db < S::DB; ++db)
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[kk][db], bop, o[db], 0, 0, 0);
     }
   };
 
   // vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding)
   constexpr int kWaitVm0 = (0x7 << 4) | (0xF << 8);
-  auto step = [&](int kt, const char* cur, char* nxt) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies of tile kt have landed
-    __syncthreads();                       // everyone's have; `nxt` is free again
+  // Iteration t: K of tile t + 1 and V of tile t are in `kcur` and `vcur`;
+  // it starts the copies of K(t + 2) into `knext` (K(t) is done) and of
+  // V(t + 1) into `vnext` (V(t - 1) is done), then runs slots 2t + 1, 2t + 2.
+  // FAST: both slots have all three parts and no diagonal chunk.
+  auto iter = [&](auto fast_tag, int t, const char* kcur, char* vcur, char* knext, char* vnext)
+      __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's copies have landed
+    __syncthreads();                       // everyone's have, and every read of the old tiles is done
     if constexpr (VB) {
-      if (kt * S::KT + S::KT > L) {        // uniform: the tile reaches past the last key
-        clear_v_tail(kt, const_cast<char*>(cur));
+      if (t * S::KT + S::KT > L) {         // uniform: the tile reaches past the last key
+        clear_v_tail(t, vcur);
         __syncthreads();
       }
     }
-    const i32x4_t ex = {__builtin_amdgcn_readlane(meta, 4), __builtin_amdgcn_readlane(meta, 5),
-                        __builtin_amdgcn_readlane(meta, 6), __builtin_amdgcn_readlane(meta, 7)};
-    if (kt + 1 < nkt) issue(kt + 1, nxt);
-    load_meta(kt + 2);
-    const int k0 = kt * S::KT;
-    if (k0 <= wlast) {
-      // both chunks' scores first, so the softmax of chunk 0 overlaps the
-      // MFMAs of chunk 1, and the softmax of chunk 1 those of chunk 0's P.V
-      const bool two = k0 + 32 <= wlast;
-      f32x16_t s0, s1;
-      scores(cur, 0, s0);
-      if (two) scores(cur, 1, s1);
-      softmax_pv(cur, ex, k0, 0, s0);
-      if (two) softmax_pv(cur, ex, k0, 1, s1);
+    int ex[4] = {0, 0, 0, 0};
+    if constexpr (!VB) {
+      ex[0] = __builtin_amdgcn_readlane(meta, 4);
+      ex[1] = __builtin_amdgcn_readlane(meta, 5);
+      ex[2] = __builtin_amdgcn_readlane(meta, 6);
+      ex[3] = __builtin_amdgcn_readlane(meta, 7);
     }
+    if (t + 2 < nkt) issue_k(t + 2, knext, 0);
+    if (t + 1 < nkt) issue_v(t + 1, vnext, 4);
+    load_meta(t + 1);
+    pre_slot(2 * t + 1, ex[0], ex[1], ph[0]);
+    if constexpr (FAST)
+      slot_fast(2 * t + 1, kcur, vcur, 0, sc[1], sc[0], ph[0], pl[0], ph[1], pl[1]);
+    else
+      slot_gen(2 * t + 1, kcur, vcur, 0, sc[1], sc[0], ph[0], pl[0], ph[1], pl[1]);
+    pre_slot(2 * t + 2, ex[2], ex[3], ph[1]);
+    if constexpr (FAST)
+      slot_fast(2 * t + 2, kcur, vcur, 1, sc[0], sc[1], ph[1], pl[1], ph[0], pl[0]);
+    else
+      slot_gen(2 * t + 2, kcur, vcur, 1, sc[0], sc[1], ph[1], pl[1], ph[0], pl[0]);
   };
+  using Fast = std::true_type;
+  using Gen = std::false_type;
+
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);    // ids of tiles 0 and 1
+  issue_k(0, kb0, 0);
+  issue_v(0, vb0, 0);
+  if (1 < nkt) issue_k(1, kb1, 4);
   load_meta(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  issue(0, lds0);
-  load_meta(1);
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(kt, lds0, lds1);
-    if (kt + 1 < nkt) step(kt + 1, lds1, lds0);
+  __syncthreads();
+  if (nch > 0) {  // S^T of chunk 0, then slot 0
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qk_mfma(k_frag(kb0, 0, ks), ks, sc[0]);
+  }
+  slot_gen(0, kb0, vb0, 1, sc[0], sc[1], ph[1], pl[1], ph[0], pl[0]);
+  // Leading iterations whose slots are all fast (chunk 2t + 3 exists and
+  // chunk 2t + 2 ends at or before the wave's first row), then the rest.
+  // Two loops rather than one with a branch per slot: the compiler would keep
+  // both sides' accumulators alive across such a branch.
+  const int n_a = max(0, (nch - 2) / 2);
+  const int n_b = wp0 >= 95 ? (wp0 - 95) / 64 + 1 : 0;
+  const int nfast = uniform(min(min(n_a, n_b), nkt));
+  for (int t = 0; t < nfast; t += 2) {
+    iter(Fast{}, t, kb1, vb0, kb0, vb1);
+    if (t + 1 < nfast) iter(Fast{}, t + 1, kb0, vb1, kb1, vb0);
+  }
+  for (int t = nfast; t < nkt; ++t) {
+    const bool odd = t & 1;
+    iter(Gen{}, t, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1);
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -2137,9 +2239,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 template <int D, int G, bool VB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_tile(
     PrefillParams p) {
-  __shared__ __align__(16) char lds0[PrefillLds<D, G>::STAGE];
-  __shared__ __align__(16) char lds1[PrefillLds<D, G>::STAGE];
-  prefill_item<D, G, VB>(p, blockIdx.x, lds0, lds1);
+  constexpr int BUF = PrefillShape<D, G>::BUF;
+  __shared__ __align__(16) char kb0[BUF];
+  __shared__ __align__(16) char kb1[BUF];
+  __shared__ __align__(16) char vb0[BUF];
+  __shared__ __align__(16) char vb1[BUF];
+  prefill_item<D, G, VB>(p, blockIdx.x, kb0, kb1, vb0, vb1);
 }
 
 // One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
@@ -2155,16 +2260,18 @@ struct MixedParams {
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_mixed(MixedParams m) {
   constexpr int DEC = DecodeLds<2, D, G>::BYTES;
-  constexpr int PRE = PrefillLds<D, G>::STAGE;
-  static_assert(4 * DEC <= PRE, "decode waves share the first prefill stage");
-  __shared__ __align__(16) char lds0[PRE];
-  __shared__ __align__(16) char lds1[PRE];
+  constexpr int BUF = PrefillShape<D, G>::BUF;
+  static_assert(2 * DEC <= BUF, "two decode waves share one prefill buffer");
+  __shared__ __align__(16) char kb0[BUF];
+  __shared__ __align__(16) char kb1[BUF];
+  __shared__ __align__(16) char vb0[BUF];
+  __shared__ __align__(16) char vb1[BUF];
   if ((int)blockIdx.x < m.n_prefill) {
-    prefill_item<D, G, false>(m.pp, blockIdx.x, lds0, lds1);
+    prefill_item<D, G, false>(m.pp, blockIdx.x, kb0, kb1, vb0, vb1);
   } else {
     const int wave = threadIdx.x >> 6;
     const int item = ((int)blockIdx.x - m.n_prefill) * 4 + wave;
-    decode_item<2, D, G>(m.dp, item, lds0 + wave * DEC);
+    decode_item<2, D, G>(m.dp, item, (wave < 2 ? kb0 : kb1) + (wave & 1) * DEC);
   }
 }
 
