@@ -1670,6 +1670,8 @@ struct PrefillParams {
   char* vh;          // fp16 V tiles [vblock][hkv][16 * D], vblock = sequence-major
   int32_t* vexp;     // scale exponents [hkv][vblocks]
   int64_t vblocks;   // blocks of all prefill sequences, each rounded up to 4
+  int items;         // prefill q tiles over all sequences (workgroups / hkv)
+  int pair_from;     // > 0: item slots >= pair_from run the lightest items in reverse
 };
 
 template <int D, int G>
@@ -1834,7 +1836,13 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int kvh = work % p.hkv;
-  const int item = work / p.hkv;
+  int item = work / p.hkv;
+  // The dispatcher gives workgroup w + (CU count) the CU of workgroup w.  With
+  // at most two workgroups per CU, the first round takes the heaviest items
+  // (latest q tiles first) and the second round the rest from the lightest
+  // up, so the two items that share a CU add up to about the same key range
+  // on every CU.  The kv head stays work % hkv (one head's K/V per XCD's L2).
+  if (p.pair_from > 0 && item >= p.pair_from) item = p.items - 1 + p.pair_from - item;
   int s, tile, ntiles;
   const int32_t* qsl = p.qsl;
   auto tiles_of = [qsl](int q) __attribute__((always_inline)) {
@@ -2313,6 +2321,18 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
   p.vh = a.ws_v;
   p.vexp = a.ws_vexp;
   p.vblocks = a.prefill_vblocks;
+  p.items = (int)a.prefill_tiles;
+  // Pair heavy with light items on a CU when the prefill workgroups fill at
+  // most two rounds of the CUs (more rounds are balanced by the dispatcher).
+  p.pair_from = 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0) {
+    const int64_t round_items = cus / c.hkv;
+    if (round_items > 0 && a.prefill_tiles > round_items && a.prefill_tiles <= 2 * round_items)
+      p.pair_from = (int)round_items;
+  }
   return p;
 }
 
