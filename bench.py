@@ -29,12 +29,13 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
 # HBM bytes one attention call moves on this workload, from rocprofv3
 # FETCH_SIZE (scaled by the factor a 1 GiB device copy needs) plus WRITE_SIZE
-# of k_decode_stream; see profiles/decode_8b_gqa_b256_traffic.md.  Reset to
-# None whenever the kernel changes until the counters are taken again.
-MEASURED_TRAFFIC_BYTES = 1_351_737_000
-# The same for the FP8 E4M3 cache variant (k_decode_stream<1,128,4>); see
-# profiles/decode_8b_gqa_b256_fp8_kv.md.
-MEASURED_TRAFFIC_BYTES_FP8 = 692_397_000
+# of k_decode_stream (2048 waves); see profiles/decode_8b_gqa_b256_traffic.md.
+# Reset to None whenever the kernel or its launch changes until the counters
+# are taken again.
+MEASURED_TRAFFIC_BYTES = 1_365_047_000
+# The same for the FP8 E4M3 cache variant (k_decode_stream<1,128,4>, 3072
+# waves); see profiles/decode_8b_gqa_b256_fp8_kv.md.
+MEASURED_TRAFFIC_BYTES_FP8 = 700_614_000
 
 
 def algorithmic_kv_bytes(w) -> int:
@@ -104,6 +105,22 @@ def prefill_flops(w) -> float:
     return total
 
 
+def make_flush(mb: int):
+    """A callable that reads `mb` MiB of scratch on the current stream (no-op for 0).
+
+    Run before every timed step so that no step finds the previous step's data
+    in the 256 MB Infinity Cache or its translations in the TLBs.  It reads
+    rather than writes: a written flush leaves dirty lines whose write-back
+    then lands inside the timed call (on the 8B GQA decode step that costs
+    +33%, against +9% for the read, and 2 ms of idle time in between changes
+    neither)."""
+    import torch
+    if mb <= 0:
+        return lambda: None
+    buf = torch.ones((mb << 20) // 4, dtype=torch.int32, device="cuda")
+    return lambda: buf.sum()
+
+
 def _timed(fn, steps, warmup, stream, flush=None):
     import torch
     for _ in range(warmup):
@@ -113,7 +130,7 @@ def _timed(fn, steps, warmup, stream, flush=None):
           for _ in range(steps)]
     for i in range(steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush()
         a, b = ev[i]
         a.record(stream)
         fn()
@@ -146,7 +163,8 @@ def run_mixed(args):
     st.run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    mixed_ms = _timed(st.attend, args.steps, args.warmup, stream)
+    flush = make_flush(args.flush_mb)
+    mixed_ms = _timed(st.attend, args.steps, args.warmup, stream, flush)
     # the chunk alone: same call restricted to the prefill sequence
     s = int(np.argmax(w.q_len))
     r0, r1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
@@ -164,7 +182,7 @@ def run_mixed(args):
         L.paged_attention_mixed(st.cache, out, q, d_qsl, d_len, sub_qsl, sub_len, d_bt, w.scale,
                                 ws)
 
-    pre_ms = _timed(prefill, args.steps, args.warmup, stream)
+    pre_ms = _timed(prefill, args.steps, args.warmup, stream, flush)
     torch.cuda.synchronize()
     assert torch.equal(out, st.out[r0:r1]), "prefill-alone rows differ from the mixed call's"
     flops = prefill_flops(w)
@@ -177,7 +195,8 @@ def run_mixed(args):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed_mean,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "8B GQA mixed step: 98 decode rows (contexts U[64,4096]) + one "
-                               "1950-token prefill chunk on 1048 cached tokens, 2048 new tokens"},
+                               "1950-token prefill chunk on 1048 cached tokens, 2048 new tokens",
+                   "flush_mb_read_before_each_step": args.flush_mb},
         "prefill_ms": pre_mean,
         "prefill_gflop": flops / 1e9,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
@@ -293,11 +312,12 @@ def main() -> None:
                          "sequence (speculative decoding); all but decode are reported "
                          "separately")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flush-mb", type=int, default=0,
-                    help="write this many MiB of scratch between timed steps (0 = back to back)")
+    ap.add_argument("--flush-mb", type=int, default=1024,
+                    help="read this many MiB of scratch before every timed step, so that no "
+                         "step reuses the last one's cached data (0 = back to back)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: run with --gpus 1"}))
         sys.exit(2)
 
     if args.workload == "prefix-cache":
@@ -335,27 +355,32 @@ def main() -> None:
     st.prepare_step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    flush = torch.empty(max(args.flush_mb, 1) << 20, dtype=torch.uint8, device="cuda")
+    flush = make_flush(args.flush_mb)
 
     for _ in range(args.warmup):
         st.run()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if args.flush_mb:
-            flush.fill_(i & 0xFF)
-        a, b, c = ev[i]
-        a.record(stream)
-        st.copy_and_write()
-        b.record(stream)
-        st.attend()
-        c.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    def timed_loop(flush_fn):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush_fn()
+            a, b, c = ev[i]
+            a.record(stream)
+            st.copy_and_write()
+            b.record(stream)
+            st.attend()
+            c.record(stream)
+        torch.cuda.synchronize()
+        return ev, time.perf_counter() - t0
+
+    ev, wall = timed_loop(flush)
+    # the same steps back to back, for reference (cache state left by the last step)
+    ev_warm, _ = timed_loop(lambda: None) if args.flush_mb > 0 else (ev, wall)
+    attn_warm = float(np.mean([b.elapsed_time(c) for _, b, c in ev_warm]))
 
     step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
     attn_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
@@ -400,9 +425,11 @@ def main() -> None:
             "global_batch": w.batch,
             "sum_context_tokens": int(w.seq_lens.sum()),
             "parallelism": "none (1 GPU)",
-            "flush_mb_between_steps": args.flush_mb,
+            "flush_mb_read_before_each_step": args.flush_mb,
         },
         "attention_ms": attn_mean,
+        "attention_ms_back_to_back": attn_warm,
+        "pct_hbm_peak_back_to_back": 100.0 * alg / (attn_warm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "attention_ms_p10_p90": [float(np.percentile(attn_ms, 10)), float(np.percentile(attn_ms, 90))],
         "write_ms": float((step_ms - attn_ms).mean()),
         "hbm_gbps": achieved,

@@ -1566,12 +1566,15 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
   else if (dtype_bytes == 2 && D == 64) { PKV_SLOTS(2, 64) }
   else if (dtype_bytes == 2 && D == 128) { PKV_SLOTS(2, 128) }
 #undef PKV_SLOTS
-  // bf16 / fp32 caches: one wave per SIMD.  Measured on MI355X (8B GQA batch
-  // 256): 0.260 ms against 0.269 ms with two waves per SIMD, whose extra
-  // requests in flight HBM does not serve any faster.  fp8 caches move half
-  // the bytes per step for more arithmetic: two waves per SIMD hide each
-  // step's chain (0.157 ms against 0.208 with one and 0.166 with three).
-  const int per_cu = dtype_bytes == 1 ? 8 : 4;
+  // Measured on MI355X (8B GQA batch 256, 1 GiB of other data read before
+  // every call so that neither the Infinity Cache nor the TLBs hold the last
+  // call's blocks):
+  //  - bf16: two waves per SIMD, 0.267 ms against 0.284 ms with one, whose
+  //    single chain of requests hides those misses less well (back to back,
+  //    with the blocks still cached, one wave is the faster: 0.260 vs 0.267);
+  //  - fp8 (half the bytes per step, more arithmetic): three waves per SIMD,
+  //    0.164 ms against 0.175 with two (back to back: 0.161 vs 0.151).
+  const int per_cu = dtype_bytes == 1 ? 12 : 8;
   return (nb < per_cu ? nb : per_cu) * cus;
 }
 
