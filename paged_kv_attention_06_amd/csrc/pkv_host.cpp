@@ -162,6 +162,16 @@ bool prefill_reads_bf16_v(const Plan& p) {
   return p.max_prefill_q <= 64;
 }
 
+// Pure prefill calls whose sequences all have at most 32 / G query rows
+// (speculative verify, short chunks) run k_prefill_mq, whose MFMA rows are
+// the G heads x 32 / G positions of one sequence.  PKV_PREFILL_MQ=0 sends
+// them to the tile kernel instead.
+bool prefill_multi_query(const Plan& p, int group) {
+  if (p.prefill_tiles == 0 || p.decode_units > 0 || p.max_prefill_q > 32 / group) return false;
+  const char* e = std::getenv("PKV_PREFILL_MQ");
+  return !(e && std::strcmp(e, "0") == 0);
+}
+
 // Decode rows without prefill rows use the stream kernel unless
 // PKV_DECODE_SPLIT=units asks for fixed 256-token partitions plus a merge
 // launch (the path mixed batches use).
@@ -256,6 +266,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   for (int k = 0; k < pkv::kPartClasses; ++k) a.class_start[k + 1] = a.class_start[k] + plan.class_count[k];
   a.prefill_tiles = plan.prefill_tiles;
   a.prefill_v_bf16 = prefill_reads_bf16_v(plan);
+  a.prefill_mq = prefill_multi_query(plan, num_q_heads / c.hkv);
   a.prefill_seqs = plan.prefill_seqs;
   a.prefill_vblocks = plan.prefill_vblocks;
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;

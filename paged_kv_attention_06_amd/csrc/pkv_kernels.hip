@@ -2258,6 +2258,225 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   prefill_item<D, G, VB>(p, blockIdx.x, kb0, kb1, vb0, vb1);
 }
 
+// ---- Multi-query rows: pure prefill calls whose sequences all have at most
+// 32 / G query rows (speculative verify, short chunks).  One workgroup per
+// (sequence, kv head).  The 32 rows of every MFMA are the G query heads x
+// 32 / G positions, so no row is padding; wave w takes the sequence's 32-key
+// chunks w, w + 4, w + 8, ... with K and V read straight from the pool into
+// MFMA operand registers (no LDS, no barrier), and the four waves' partial
+// (max, sum, O) are merged through LDS at the end.  Operand and accumulator
+// layouts are those of k_prefill_tile's bf16-V variant: lane (h, r) of the
+// K operand reads key pi(r), pi swapping bits 2 and 3, so that the 16 S^T
+// values a lane holds are the keys 16 (i / 8) + 8 h + i % 8 that the P.V
+// operand needs; P enters as a bf16 hi + lo pair.
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_mq(
+    PrefillParams p) {
+  constexpr int NP = 32 / G;        // positions per wave
+  constexpr int KS = D / 16;        // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;        // 32-row d blocks of O^T
+  constexpr int TILE = BS * D * 2;  // bytes of one block's K (or V) tile
+  __shared__ float mg_o[4][DB * 16][64];
+  __shared__ float mg_ml[4][2][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int kvh = blockIdx.x % p.hkv;
+  const int s = blockIdx.x / p.hkv;
+  const int hq = p.hkv * G;
+  const int L = uniform(p.seq_lens[s]);
+  const int row0 = uniform(p.qsl[s]);
+  const int ql = uniform(p.qsl[s + 1]) - row0;
+  if (ql <= 0) return;                   // uniform over the workgroup
+  const int qfirst = L - ql;
+  const int h = lane >> 5;
+  const int r = lane & 31;
+  const int g = r / NP, i = r % NP;      // this lane's query row: head g, position i
+  const bool row_ok = i < ql;
+  const int lim = row_ok ? qfirst + i : -1;  // last key the row sees
+  const int head = kvh * G + g;
+  const bool neg = p.scale_log2 < 0.f;
+  const float c = fmaxf(fabsf(p.scale_log2), 1.17549435e-38f);
+
+  // Q^T operand: lane (h, r) holds q[row r][16 ks + 8 h .. + 8]; a negative
+  // scale is carried by negating q (exact), so that c > 0.
+  bf16x8_t qb[KS];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        p.q + ((size_t)(row0 + (row_ok ? i : 0)) * hq + head) * D);
+    const uint32_t flip = neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = row_ok ? qrow[2 * ks + h] : make_uint4(0, 0, 0, 0);
+      v.x ^= flip; v.y ^= flip; v.z ^= flip; v.w ^= flip;
+      qb[ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) o[db][k] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  const int pr = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+  const int nbl = (L + BS - 1) / BS;
+  const int nch = (L + 31) / 32;
+  const int32_t* bt_row = p.block_tables + (size_t)s * p.max_blocks;
+  const char* kbase = p.kv + (size_t)kvh * 2 * TILE;
+  const char* vbase = kbase + TILE;
+
+  // K and V operands of one chunk; two sets alternate so that the next
+  // chunk's loads are in flight while this one is computed.
+  struct ChunkRegs {
+    uint4 a[KS];      // K operand of key pi(r), d-granule 2 ks + h
+    uint4 v[2][DB];   // V^T operand of block kk: granule (key group h, d = 32 db + r)
+  };
+  // Block ids of chunk ch (clamped to the last valid entry past the table's
+  // end: those keys are masked and their V zeroed).
+  auto chunk_ids = [&](int ch, int& b0, int& b1) __attribute__((always_inline)) {
+    const int e = min(2 * ch, nbl - 1);
+    b0 = uniform(bt_row[e]);
+    b1 = uniform(bt_row[min(e + 1, nbl - 1)]);
+  };
+  auto load_chunk = [&](ChunkRegs& cr, int b0, int b1) __attribute__((always_inline)) {
+    const char* kp = kbase + (size_t)((pr >> 4) ? b1 : b0) * p.block_bytes + (h * 16 + (pr & 15)) * 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cr.a[ks] = *reinterpret_cast<const uint4*>(kp + ks * 512);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const char* vp = vbase + (size_t)(kk ? b1 : b0) * p.block_bytes + (h * D + r) * 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) cr.v[kk][db] = *reinterpret_cast<const uint4*>(vp + db * 512);
+    }
+  };
+  auto compute_chunk = [&](ChunkRegs& cr, int ch) __attribute__((always_inline)) {
+    f32x16_t sacc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) sacc[k] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cr.a[ks]), qb[ks],
+                                                     sacc, 0, 0, 0);
+    const int kj = 32 * ch;
+    if (uniform(kj + 31 > qfirst)) {  // the chunk reaches the first row's position (or L)
+      const int kl = lim - (kj + 8 * h);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) sacc[k] = (16 * (k >> 3) + (k & 7) <= kl) ? sacc[k] : -INFINITY;
+      // keys at or past L (unwritten slots, blocks past the table) get a zero
+      // V, so that a zero probability never meets a NaN
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int t0 = L - (kj + 16 * kk + 8 * h);  // keys of this granule from t0 on are past L
+        if (t0 < 8) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            uint32_t w4[4] = {cr.v[kk][db].x, cr.v[kk][db].y, cr.v[kk][db].z, cr.v[kk][db].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (e >= t0) w4[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            cr.v[kk][db] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+          }
+        }
+      }
+    }
+    float mt = sacc[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) mt = __builtin_elementwise_maximum(mt, sacc[k]);
+    mt = half_swap_max(mt) * c;
+    if (mt > m_run + kRescaleSlack) {  // per lane; the rows of a wave rescale on their own
+      const float corr = __builtin_amdgcn_exp2f(m_run - mt);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[db][k] *= corr;
+      m_run = mt;
+    }
+    const float nm = -m_run;
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) {
+      const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w2], c, nm));
+      const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[2 * w2 + 1], c, nm));
+      l_run += x0 + x1;
+      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+      ph[w2] = hw;
+      pl[w2] = __builtin_bit_cast(
+          uint32_t, __builtin_convertvector((f32x2_t){x0 - bf16_lo(hw), x1 - bf16_hi(hw)}, bf16x2_t));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8_t bh = __builtin_bit_cast(
+          bf16x8_t, make_uint4(ph[4 * kk], ph[4 * kk + 1], ph[4 * kk + 2], ph[4 * kk + 3]));
+      const bf16x8_t bl = __builtin_bit_cast(
+          bf16x8_t, make_uint4(pl[4 * kk], pl[4 * kk + 1], pl[4 * kk + 2], pl[4 * kk + 3]));
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const bf16x8_t vb = __builtin_bit_cast(bf16x8_t, cr.v[kk][db]);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bh, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, bl, o[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // Chunks wave, wave + 4, ...: chunk k + 1's K/V and chunk k + 2's block ids
+  // are requested before chunk k is computed.  Past the wave's last chunk the
+  // loads repeat its last blocks (cache hits) instead of branching around
+  // them, so every iteration issues the same loads.
+  if (wave < nch) {
+    ChunkRegs ra, rb;
+    int b0, b1, n0, n1;
+    chunk_ids(wave, b0, b1);
+    load_chunk(ra, b0, b1);
+    chunk_ids(min(wave + 4, nch - 1), n0, n1);
+    for (int ch = wave; ch < nch; ch += 8) {
+      load_chunk(rb, n0, n1);
+      chunk_ids(min(ch + 8, nch - 1), b0, b1);
+      compute_chunk(ra, ch);
+      if (ch + 4 >= nch) break;
+      load_chunk(ra, b0, b1);
+      chunk_ids(min(ch + 12, nch - 1), n0, n1);
+      compute_chunk(rb, ch + 4);
+    }
+  }
+
+  // ---- merge the four waves' partials: wave w writes its own, then forms
+  // the output of d-block w (lane (h, r): row r, d = 32 w + 8 i4 + 4 h .. + 4)
+  const float l_tot = half_swap_sum(l_run);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) mg_o[wave][db * 16 + k][lane] = o[db][k];
+  mg_ml[wave][0][lane] = m_run;
+  mg_ml[wave][1][lane] = l_tot;
+  __syncthreads();
+  if (wave >= DB || !row_ok) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int sw = 0; sw < 4; ++sw) M = fmaxf(M, mg_ml[sw][0][lane]);
+  float den = 0.f, num[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) num[k] = 0.f;
+#pragma unroll
+  for (int sw = 0; sw < 4; ++sw) {
+    const float a = __builtin_amdgcn_exp2f(mg_ml[sw][0][lane] - M);
+    den = fmaf(a, mg_ml[sw][1][lane], den);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) num[k] = fmaf(a, mg_o[sw][wave * 16 + k][lane], num[k]);
+  }
+  const float inv = 1.f / den;
+  float* orow = p.out + (((size_t)row0 + i) * hq + head) * D;
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const int d = 32 * wave + 8 * i4 + 4 * h;
+    *reinterpret_cast<float4*>(orow + d) =
+        make_float4(num[4 * i4] * inv, num[4 * i4 + 1] * inv, num[4 * i4 + 2] * inv,
+                    num[4 * i4 + 3] * inv);
+  }
+}
+
 // One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
 // (compute-bound, MFMA) and the rest run four decode items each, one per
 // wave (bandwidth-bound), so both kinds of work share the CUs instead of
@@ -2339,11 +2558,29 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
   return p;
 }
 
+template <int D>
+static hipError_t prefill_mq(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
+  const dim3 g((unsigned)grid), b(256);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_prefill_mq<D, 1>), g, b, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill_mq<D, 2>), g, b, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill_mq<D, 4>), g, b, 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   if (a.prefill_tiles == 0) return hipSuccess;
   if (c.dtype_bytes != 2) return hipErrorInvalidValue;
   const PrefillParams p = make_prefill_params(c, a);
   const int G = a.hq / c.hkv;
+  if (a.prefill_mq) {  // every sequence has at most 32 / G query rows
+    const int64_t grid = (int64_t)a.num_seqs * c.hkv;
+    if (c.head_size == 128) return prefill_mq<128>(G, p, grid, stream);
+    if (c.head_size == 64) return prefill_mq<64>(G, p, grid, stream);
+    return hipErrorInvalidValue;
+  }
   const int64_t grid = a.prefill_tiles * c.hkv;
   if (a.prefill_v_bf16) {
     if (c.head_size == 128) return prefill_g<128, true>(G, p, grid, stream);

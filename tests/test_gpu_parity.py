@@ -290,6 +290,35 @@ def test_prefill_chunk_rows_dense_sample():
     _check_attention(got, ref, "bf16", "prefill chunk rows")
 
 
+# ------------------------------------------------- multi-query rows (k_prefill_mq)
+@pytest.mark.parametrize("G,D", [(4, 128), (2, 128), (1, 128), (4, 64), (1, 64)])
+def test_multi_query_rows(G, D, monkeypatch):
+    """Pure prefill calls whose sequences all have at most 32 / G query rows
+    go to k_prefill_mq (MFMA rows = the G heads x 32 / G positions).  Short
+    and long histories, a sequence inside one block, q_len from 2 to 32 / G;
+    every row against the oracle, and the same call through the tile kernel
+    (PKV_PREFILL_MQ=0)."""
+    rng = np.random.default_rng(90 + G + D)
+    hkv = 4
+    maxq = 32 // G
+    ql = np.concatenate([[2, maxq, 3], rng.integers(2, maxq + 1, 9)]).astype(np.int32)
+    hist = np.concatenate([[5, 0, 1000], rng.integers(0, 700, 9)]).astype(np.int32)
+    hist[1] = max(0, 9 - int(ql[1]))  # L = 9 or q_len: one partly filled block
+    streams = [np.random.default_rng(91 + G + D + x) for x in range(4)]
+    pool = int(1.25 * sum((int(a) + int(b) + 15) // 16 for a, b in zip(hist, ql))) + 8
+    w = workloads._build(4, "multi-query rows", "bf16", hkv * G, hkv, D, D ** -0.5,
+                         hist, ql, pool, streams)
+    _announce(f"multi-query rows G={G} D={D}: q_len={w.q_len.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"multi-query G={G} D={D}")
+    monkeypatch.setenv("PKV_PREFILL_MQ", "0")
+    st.out.fill_(0)
+    st.attend()
+    torch.cuda.synchronize()
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"tile kernel G={G} D={D}")
+
+
 # ------------------------------------------------------------- FP8 KV cache
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_fp8_small_workload_full_parity(cfg):
