@@ -253,6 +253,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.block_tables = block_tables;
   a.max_blocks = max_blocks;
   a.seq_lens = seq_lens;
+  a.h_seq_lens = h_seq_lens;
   a.query_start_loc = mixed ? qsl : nullptr;
   a.num_seqs = num_seqs;
   a.scale = scale * c.k_scale;  // an fp8 cache's K scale folds into the score scale

@@ -47,6 +47,7 @@ struct AttnDesc {
   const int32_t* block_tables;
   int max_blocks;
   const int32_t* seq_lens;
+  const int32_t* h_seq_lens;       // host copy (valid during the call)
   const int32_t* query_start_loc;  // nullptr: pure decode, row s = sequence s
   int num_seqs;
   float scale;

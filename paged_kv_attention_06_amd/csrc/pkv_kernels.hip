@@ -16,6 +16,8 @@
 // granule) and a V tile with lane = d (64 lanes x 16 B contiguous), both as
 // whole 16-byte loads, so no transpose through LDS is needed.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "pkv_internal.h"
@@ -2269,9 +2271,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // K operand reads key pi(r), pi swapping bits 2 and 3, so that the 16 S^T
 // values a lane holds are the keys 16 (i / 8) + 8 h + i % 8 that the P.V
 // operand needs; P enters as a bf16 hi + lo pair.
+// Sequences in the order their workgroups start: longest first, so that the
+// long ones do not start in the last round.  n = 0: index order.
+constexpr int kMqOrderMax = 1024;
+struct MqParams {
+  PrefillParams p;
+  int n;
+  uint16_t order[kMqOrderMax];
+};
+
 template <int D, int G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_mq(
-    PrefillParams p) {
+    MqParams mp) {
+  const PrefillParams& p = mp.p;
   constexpr int NP = 32 / G;        // positions per wave
   constexpr int KS = D / 16;        // MFMA k-steps over the head dim
   constexpr int DB = D / 32;        // 32-row d blocks of O^T
@@ -2282,7 +2294,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int kvh = blockIdx.x % p.hkv;
-  const int s = blockIdx.x / p.hkv;
+  const int rank = blockIdx.x / p.hkv;
+  const int s = mp.n > 0 ? (int)mp.order[rank] : rank;
   const int hq = p.hkv * G;
   const int L = uniform(p.seq_lens[s]);
   const int row0 = uniform(p.qsl[s]);
@@ -2559,12 +2572,12 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
 }
 
 template <int D>
-static hipError_t prefill_mq(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
+static hipError_t prefill_mq(int G, const MqParams& mp, int64_t grid, hipStream_t stream) {
   const dim3 g((unsigned)grid), b(256);
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_prefill_mq<D, 1>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_prefill_mq<D, 2>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_prefill_mq<D, 4>), g, b, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((k_prefill_mq<D, 1>), g, b, 0, stream, mp); break;
+    case 2: hipLaunchKernelGGL((k_prefill_mq<D, 2>), g, b, 0, stream, mp); break;
+    case 4: hipLaunchKernelGGL((k_prefill_mq<D, 4>), g, b, 0, stream, mp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2576,9 +2589,19 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
   const PrefillParams p = make_prefill_params(c, a);
   const int G = a.hq / c.hkv;
   if (a.prefill_mq) {  // every sequence has at most 32 / G query rows
+    MqParams mp;
+    mp.p = p;
+    mp.n = 0;
+    if (a.h_seq_lens && a.num_seqs <= kMqOrderMax) {  // longest sequences start first
+      for (int i = 0; i < a.num_seqs; ++i) mp.order[i] = (uint16_t)i;
+      std::stable_sort(mp.order, mp.order + a.num_seqs, [&a](uint16_t x, uint16_t y) {
+        return a.h_seq_lens[x] > a.h_seq_lens[y];
+      });
+      mp.n = a.num_seqs;
+    }
     const int64_t grid = (int64_t)a.num_seqs * c.hkv;
-    if (c.head_size == 128) return prefill_mq<128>(G, p, grid, stream);
-    if (c.head_size == 64) return prefill_mq<64>(G, p, grid, stream);
+    if (c.head_size == 128) return prefill_mq<128>(G, mp, grid, stream);
+    if (c.head_size == 64) return prefill_mq<64>(G, mp, grid, stream);
     return hipErrorInvalidValue;
   }
   const int64_t grid = a.prefill_tiles * c.hkv;
