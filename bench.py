@@ -36,6 +36,9 @@ MEASURED_TRAFFIC_BYTES = 1_365_047_000
 # The same for the FP8 E4M3 cache variant (k_decode_stream<1,128,4>, 3072
 # waves); see profiles/decode_8b_gqa_b256_fp8_kv.md.
 MEASURED_TRAFFIC_BYTES_FP8 = 700_614_000
+# The same for the speculative-verify batch (k_prefill_mq<128,4>); see
+# profiles/verify_8b_gqa_b256_k3_multi_query.md.
+MEASURED_TRAFFIC_BYTES_VERIFY = 1_486_721_000
 
 
 def algorithmic_kv_bytes(w) -> int:
@@ -445,9 +448,10 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if (verify or other) else (MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
-                                                       MEASURED_TRAFFIC_BYTES),
-            "kernel": ("paged_attention_mixed (k_prefill_tile, bf16 V)" if verify else
+            "traffic": None if other else (MEASURED_TRAFFIC_BYTES_VERIFY if verify else
+                                           MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
+                                           MEASURED_TRAFFIC_BYTES),
+            "kernel": ("paged_attention_mixed (k_prefill_mq)" if verify else
                        "paged_attention_decode (k_decode_stream, one launch)"),
             "algorithmic_bytes_per_launch": alg,
         },
