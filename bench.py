@@ -152,7 +152,8 @@ def copy_bandwidth(nbytes=1 << 30):
 
 
 def run_mixed(args):
-    """Config 4: the whole mixed call, and the prefill chunk alone."""
+    """The 8B GQA mixed step (98 decode rows + a 1950-row chunk): the whole
+    mixed call, and the prefill chunk alone."""
     import torch
 
     import workloads

@@ -46,14 +46,14 @@ def _check_attention(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str):
 def test_small_workload_full_parity(cfg):
     """Whole pool bit-exact and every output row within tolerance."""
     w = workloads.small(cfg)
-    _announce(f"small config {cfg}: B={w.batch} T={w.num_tokens} L={w.seq_lens.tolist()}")
+    _announce(f"small {w.name}: B={w.batch} T={w.num_tokens} L={w.seq_lens.tolist()}")
     st = gpu_step.run_workload(w)
     ref = scenario.run_step(w)
     assert np.array_equal(st.h_slots, ref["slots"])
     assert np.array_equal(st.h_cow, ref["cow_pairs"])
     pool = st.pool_codes()
     assert np.array_equal(pool, ref["pool"]), "pool differs from the oracle's"
-    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"small config {cfg}")
+    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"small {w.name}")
 
 
 def _sample_seqs(w, k=6, seed=0):
@@ -71,7 +71,7 @@ def test_full_size_sampled_parity(cfg):
     """Full-size workload in the bench's launch configuration; sampled rows
     against the oracle, plus the step's written slots and COW copies."""
     w = workloads.make(cfg)
-    _announce(f"full config {cfg}: B={w.batch} T={w.num_tokens} blocks={w.num_blocks}")
+    _announce(f"full {w.name}: B={w.batch} T={w.num_tokens} blocks={w.num_blocks}")
     st = gpu_step.run_workload(w)
     out = st.out.cpu().numpy()
     assert np.all(np.isfinite(out)), "non-finite output"
@@ -83,7 +83,7 @@ def test_full_size_sampled_parity(cfg):
         ref = scenario.sequence_attention(w, s, rows)
         got.append(out[qsl[s] + np.asarray(rows)])
         want.append(ref)
-    _check_attention(np.concatenate(got), np.concatenate(want), w.dtype, f"full config {cfg}")
+    _check_attention(np.concatenate(got), np.concatenate(want), w.dtype, f"full {w.name}")
 
     # the step's written tokens sit at the oracle's slots with their drawn values
     tabs = scenario.build_tables(w, with_pool=False)
@@ -116,7 +116,7 @@ def test_decode_is_deterministic_and_layout_invariant():
     """Two runs give identical bits; moving every block to another physical
     id (a different free order) gives identical bits too."""
     w = workloads.small(3)
-    _announce("determinism / block permutation, small config 3")
+    _announce("determinism / block permutation, small 8B GQA decode")
     a = gpu_step.run_workload(w).out.cpu().numpy()
     b = gpu_step.run_workload(w).out.cpu().numpy()
     assert np.array_equal(a, b)
@@ -244,10 +244,10 @@ def test_fixed_partition_decode_path(cfg, monkeypatch):
     batches."""
     monkeypatch.setenv("PKV_DECODE_SPLIT", "units")
     w = workloads.small(cfg)
-    _announce(f"units split, small config {cfg}")
+    _announce(f"units split, small {w.name}")
     st = gpu_step.run_workload(w)
     ref = scenario.run_step(w)
-    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"units split config {cfg}")
+    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"units split {w.name}")
 
 
 def test_workspace_reused_with_new_queries():
@@ -325,24 +325,24 @@ def test_fp8_small_workload_full_parity(cfg):
     """FP8 E4M3 cache: quantized writes give the oracle's pool bit for bit
     (every code and untouched byte), attention within the bars."""
     w = workloads.make_fp8(cfg, small_size=True)
-    _announce(f"fp8 small config {cfg}: B={w.batch} L={w.seq_lens.tolist()}")
+    _announce(f"fp8 small {w.name}: B={w.batch} L={w.seq_lens.tolist()}")
     st = gpu_step.run_workload(w)
     ref = scenario.run_step(w)
     assert np.array_equal(st.pool_codes(), ref["pool"]), "fp8 pool differs from the oracle's"
-    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"fp8 small config {cfg}")
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"fp8 small {w.name}")
 
 
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_fp8_full_size_sampled_parity(cfg):
     w = workloads.make_fp8(cfg)
-    _announce(f"fp8 full config {cfg}: B={w.batch} blocks={w.num_blocks}")
+    _announce(f"fp8 full {w.name}: B={w.batch} blocks={w.num_blocks}")
     st = gpu_step.run_workload(w)
     out = st.out.cpu().numpy()
     assert np.all(np.isfinite(out))
     rows = _sample_seqs(w)
     want = np.concatenate([scenario.sequence_attention(w, s) for s in rows])
     got = np.concatenate([out[s:s + 1] for s in rows])
-    _check_attention(got, want, "bf16", f"fp8 full config {cfg}")
+    _check_attention(got, want, "bf16", f"fp8 full {w.name}")
 
 
 def test_fp8_every_code_decodes_exactly():

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_block_bytes_per_config(cfg):
+def test_block_bytes_per_workload(cfg):
     w = workloads.small(cfg)
     d = P.descriptor(7, w.num_kv_heads, w.head_size, P.PKV_F32 if w.dtype == "f32" else P.PKV_BF16)
     assert P.pkv_block_bytes(d) == po.block_bytes(16, w.num_kv_heads, w.head_size, w.dtype_bytes)

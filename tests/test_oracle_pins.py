@@ -235,7 +235,7 @@ def test_block_permutation_invariance():
 
 
 def test_brute_force_tiny_decode():
-    """Config 1 recomputed with scalar Python loops and math.exp."""
+    """The tiny fp32 decode workload recomputed with scalar Python loops and math.exp."""
     w = workloads.make(1)
     st = scenario.run_step(w)
     qsl = w.query_start_loc
@@ -318,7 +318,7 @@ def test_empty_sequence_gives_zeros():
     assert np.all(out == 0)
 
 
-def test_config5_forks_all_copy_on_write():
+def test_13b_prefix_forks_all_copy_on_write():
     w = workloads.small(5)
     st = scenario.build_tables(w, with_pool=False)
     n_fork = int((w.fork_of >= 0).sum())

@@ -24,7 +24,7 @@ Five workloads, all with 16-token blocks:
 Every sequence appends ``q_len`` new tokens in the step (1 for decode) on
 top of ``hist_len`` cached ones, so its length is hist_len + q_len.
 
-Random streams: numpy SeedSequence(config_id + 1000 * seed).spawn(4) ->
+Random streams: numpy SeedSequence(workload_id + 1000 * seed).spawn(4) ->
 (lengths, physical block order, values, spare).  Values are drawn in float32
 and rounded to nearest-even bf16 where the workload is bf16.
 """
@@ -45,7 +45,7 @@ FP8_SCALE = 1.0 / 64.0
 
 @dataclass
 class Workload:
-    config_id: int
+    workload_id: int
     name: str
     dtype: str                  # "f32" | "bf16"
     num_q_heads: int
@@ -130,7 +130,7 @@ def _pool_size(lengths, factor: float, extra_blocks: int = 0) -> int:
     return int(np.ceil(factor * need))
 
 
-def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, scale: float,
+def _build(workload_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, scale: float,
            hist_len, q_len, num_blocks: int, streams, fork_of=None, prompt_len=(),
            owner_ref=False, extra=None, values: bool = True, cache_dtype: str = "",
            kv_scale: float = 1.0) -> Workload:
@@ -148,7 +148,7 @@ def _build(config_id: int, name: str, dtype: str, Hq: int, Hkv: int, D: int, sca
     n_hist = int(hist_start[-1])
     n_prompt = int(prompt_start[-1])
     w = Workload(
-        config_id=config_id, name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv,
+        workload_id=workload_id, name=name, dtype=dtype, num_q_heads=Hq, num_kv_heads=Hkv,
         head_size=D, scale=scale, num_blocks=num_blocks, free_order=free_order,
         hist_len=hist_len, q_len=q_len, fork_of=fork_of, prompt_len=prompt_len,
         prompt_owner_keeps_ref=owner_ref,
@@ -172,8 +172,8 @@ def make_verify(k: int = 3, seed: int = 0, small_size: bool = False) -> Workload
     """Speculative-decoding verify step on the 8B GQA decode batch: every
     sequence appends its last accepted token plus k draft tokens and queries
     all k + 1 positions (causal), as the pages' verify pass does (k = 3 in
-    their n-gram example).  Lengths, pool and values are drawn like config
-    3 (batch 256, or 12 short sequences with small_size)."""
+    their n-gram example).  Lengths, pool and values are drawn like the 8B
+    GQA decode workload (batch 256, or 12 short sequences with small_size)."""
     streams = [np.random.default_rng(x)
                for x in np.random.SeedSequence(20_000 + 1000 * seed + 10 * small_size).spawn(4)]
     r_len = streams[0]
@@ -190,11 +190,11 @@ def make_verify(k: int = 3, seed: int = 0, small_size: bool = False) -> Workload
                   128, 128 ** -0.5, L - (k + 1), np.full(B, k + 1, np.int32), pool, streams)
 
 
-def make_fp8(config_id: int, seed: int = 0, small_size: bool = False) -> Workload:
-    """A bf16 workload (configs 2, 3 or 5, full or small) whose KV cache is
+def make_fp8(workload_id: int, seed: int = 0, small_size: bool = False) -> Workload:
+    """A bf16 workload (2, 3 or 5, full or small) whose KV cache is
     FP8 E4M3 with K and V scales of 1/64: same lengths, blocks and drawn
     values; the cache stores them quantized."""
-    w = small(config_id, seed) if small_size else make(config_id, seed)
+    w = small(workload_id, seed) if small_size else make(workload_id, seed)
     assert w.dtype == "bf16"
     w.name = w.name + " (fp8 KV)"
     w.cache_dtype = "fp8"
@@ -203,34 +203,34 @@ def make_fp8(config_id: int, seed: int = 0, small_size: bool = False) -> Workloa
     return w
 
 
-def make(config_id: int, seed: int = 0, batch: int | None = None, values: bool = True) -> Workload:
-    """The workload of one configuration.  ``batch`` (optional) keeps the
+def make(workload_id: int, seed: int = 0, batch: int | None = None, values: bool = True) -> Workload:
+    """Workload ``workload_id`` of the list above.  ``batch`` (optional) keeps the
     shape and length distribution but draws fewer sequences, for quick runs.
     ``values=False`` skips drawing K/V/Q (zeros instead); lengths and block
     order are unchanged."""
-    streams = np.random.SeedSequence(config_id + 1000 * seed).spawn(4)
+    streams = np.random.SeedSequence(workload_id + 1000 * seed).spawn(4)
     streams = [np.random.default_rng(s) for s in streams]
     r_len = streams[0]
 
-    if config_id == 1:
+    if workload_id == 1:
         L = np.array([5, 16, 17, 40], np.int32)
         return _build(1, "tiny decode", "f32", 4, 4, 64, 1.0 / 8.0, L - 1, np.ones(4, np.int32),
                       64, streams, values=values)
 
-    if config_id == 2:
+    if workload_id == 2:
         B = batch or 64
         L = r_len.integers(128, 2048, size=B, endpoint=True).astype(np.int32)
         return _build(2, "7B MHA decode", "bf16", 32, 32, 128, 128 ** -0.5, L - 1,
                       np.ones(B, np.int32), _pool_size(L, 1.25), streams, values=values)
 
-    if config_id == 3:
+    if workload_id == 3:
         B = batch or 256
         L = np.rint(r_len.lognormal(np.log(800.0), 1.0, size=B))
         L = np.clip(L, 16, 8192).astype(np.int32)
         return _build(3, "8B GQA decode", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
                       np.ones(B, np.int32), 200_000, streams, values=values)
 
-    if config_id == 4:
+    if workload_id == 4:
         n_dec = 98 if batch is None else max(batch - 1, 1)
         L_dec = r_len.integers(64, 4096, size=n_dec, endpoint=True).astype(np.int32)
         chunk, cached = 1950, 1048
@@ -239,7 +239,7 @@ def make(config_id: int, seed: int = 0, batch: int | None = None, values: bool =
         return _build(4, "mixed chunked prefill + decode", "bf16", 32, 8, 128, 128 ** -0.5,
                       hist, qlen, _pool_size(hist + qlen, 1.25), streams, values=values)
 
-    if config_id == 5:
+    if workload_id == 5:
         n_fork = 16 if batch is None else max(batch // 2, 1)
         n_ind = 16 if batch is None else max(batch - n_fork, 1)
         prompt = 1032
@@ -253,22 +253,22 @@ def make(config_id: int, seed: int = 0, batch: int | None = None, values: bool =
                       128 ** -0.5, hist, qlen, _pool_size(lengths, 1.25, extra_blocks=n_fork),
                       streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True, values=values)
 
-    raise ValueError(f"unknown config {config_id}")
+    raise ValueError(f"unknown workload {workload_id}")
 
 
-def small(config_id: int, seed: int = 0) -> Workload:
+def small(workload_id: int, seed: int = 0) -> Workload:
     """A reduced workload of the same family that the oracle finishes in
     seconds: same head shapes and distributions, fewer and shorter seqs."""
     streams = [np.random.default_rng(s)
-               for s in np.random.SeedSequence(10_000 + config_id + 1000 * seed).spawn(4)]
+               for s in np.random.SeedSequence(10_000 + workload_id + 1000 * seed).spawn(4)]
     r_len = streams[0]
-    if config_id == 1:
+    if workload_id == 1:
         return make(1, seed)
-    if config_id == 2:
+    if workload_id == 2:
         L = r_len.integers(1, 300, size=6, endpoint=True).astype(np.int32)
         return _build(2, "7B MHA decode (small)", "bf16", 32, 32, 128, 128 ** -0.5, L - 1,
                       np.ones(6, np.int32), _pool_size(L, 1.25), streams)
-    if config_id == 3:
+    if workload_id == 3:
         L = np.clip(np.rint(r_len.lognormal(np.log(120.0), 1.0, size=12)), 1, 900).astype(np.int32)
         L[0] = 1
         L[1] = 16
@@ -276,13 +276,13 @@ def small(config_id: int, seed: int = 0) -> Workload:
         L[3] = 513
         return _build(3, "8B GQA decode (small)", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
                       np.ones(12, np.int32), 4000, streams)
-    if config_id == 4:
+    if workload_id == 4:
         L_dec = r_len.integers(1, 400, size=5, endpoint=True).astype(np.int32)
         hist = np.concatenate([L_dec - 1, [37]]).astype(np.int32)
         qlen = np.concatenate([np.ones(5, np.int32), [150]]).astype(np.int32)
         return _build(4, "mixed step (small)", "bf16", 32, 8, 128, 128 ** -0.5, hist, qlen,
                       _pool_size(hist + qlen, 1.25), streams)
-    if config_id == 5:
+    if workload_id == 5:
         prompt = 40
         L_ind = r_len.integers(1, 600, size=3, endpoint=True).astype(np.int32)
         hist = np.concatenate([np.full(3, prompt, np.int32), L_ind - 1]).astype(np.int32)
@@ -290,4 +290,4 @@ def small(config_id: int, seed: int = 0) -> Workload:
         return _build(5, "13B MHA prefix sharing (small)", "bf16", 40, 40, 128, 128 ** -0.5,
                       hist, np.ones(6, np.int32), _pool_size(list(L_ind) + [prompt], 1.25, 3),
                       streams, fork_of=fork_of, prompt_len=[prompt], owner_ref=True)
-    raise ValueError(config_id)
+    raise ValueError(workload_id)
