@@ -202,6 +202,8 @@ def run_mixed(args):
                                "1950-token prefill chunk on 1048 cached tokens, 2048 new tokens",
                    "flush_mb_read_before_each_step": args.flush_mb},
         "prefill_ms": pre_mean,
+        "prefill_ms_median_p10_p90": [float(np.median(pre_ms)), float(np.percentile(pre_ms, 10)),
+                                      float(np.percentile(pre_ms, 90))],
         "prefill_gflop": flops / 1e9,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": tflops / 2500.0, "traffic": None,
@@ -434,6 +436,7 @@ def main() -> None:
         "attention_ms": attn_mean,
         "attention_ms_back_to_back": attn_warm,
         "pct_hbm_peak_back_to_back": 100.0 * alg / (attn_warm * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "attention_ms_median": float(np.median(attn_ms)),
         "attention_ms_p10_p90": [float(np.percentile(attn_ms, 10)), float(np.percentile(attn_ms, 90))],
         "write_ms": float((step_ms - attn_ms).mean()),
         "hbm_gbps": achieved,
