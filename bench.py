@@ -310,7 +310,7 @@ def main() -> None:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify", "swap",
-                                           "prefix-cache", "decode-7b", "decode-13b"],
+                                           "prefix-cache", "decode-7b", "decode-13b", "tiny"],
                     default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
                          "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
@@ -349,7 +349,7 @@ def main() -> None:
 
     fp8 = args.workload == "decode-fp8"
     verify = args.workload == "verify"
-    other = {"decode-7b": 2, "decode-13b": 5}.get(args.workload)
+    other = {"decode-7b": 2, "decode-13b": 5, "tiny": 1}.get(args.workload)
     if fp8:
         w = workloads.make_fp8(3)
     elif verify:
@@ -398,7 +398,8 @@ def main() -> None:
 
     rec = {
         "metric": (METRIC if not (fp8 or verify or other) else
-                   {2: "decode attention tokens/s & achieved HBM GB/s (% of peak), 7B-MHA batch 64",
+                   {1: "decode step latency (launch-bound): 4 fp32 sequences, head 64",
+                    2: "decode attention tokens/s & achieved HBM GB/s (% of peak), 7B-MHA batch 64",
                     5: "decode attention tokens/s & achieved HBM GB/s (% of peak), 13B-MHA batch "
                        "32, shared prefix + long context"}[other] if other else
                    "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256, "
@@ -412,10 +413,13 @@ def main() -> None:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 cache, bf16 q, f32 accumulate" if fp8 else "bf16",
+        "dtype": ("fp8-e4m3 cache, bf16 q, f32 accumulate" if fp8 else
+                  "f32" if other == 1 else "bf16"),
         "data": "synthetic",
         "config": {
-            "workload": ({2: "Llama-7B-shaped MHA decode: 32 q / 32 kv heads, head 128, bf16 "
+            "workload": ({1: "tiny decode: 4 sequences of 5, 16, 17, 40 tokens, 4 q = 4 kv heads, "
+                             "head 64, fp32 U[-1,1], 64-block pool",
+                          2: "Llama-7B-shaped MHA decode: 32 q / 32 kv heads, head 128, bf16 "
                              "N(0,1), batch 64, contexts U[128, 2048], pool 1.25x the blocks "
                              "needed, shuffled",
                           5: "13B-shaped MHA decode: 40 / 40 heads, head 128, bf16 N(0,1), "
