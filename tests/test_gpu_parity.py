@@ -319,6 +319,23 @@ def test_multi_query_rows(G, D, monkeypatch):
     _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"tile kernel G={G} D={D}")
 
 
+def test_multi_query_rows_many_sequences():
+    """More sequences than the kernel arguments' longest-first order holds
+    (1024): the workgroups take the sequences in index order instead."""
+    rng = np.random.default_rng(97)
+    n = 1100
+    ql = rng.integers(2, 9, n).astype(np.int32)
+    hist = rng.integers(0, 60, n).astype(np.int32)
+    streams = [np.random.default_rng(98 + x) for x in range(4)]
+    pool = int(1.25 * sum((int(a) + int(b) + 15) // 16 for a, b in zip(hist, ql))) + 8
+    w = workloads._build(4, "multi-query rows, 1100 sequences", "bf16", 16, 4, 64, 64 ** -0.5,
+                         hist, ql, pool, streams)
+    _announce(f"multi-query rows, {n} sequences")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", "multi-query, 1100 sequences")
+
+
 # ------------------------------------------------------------- FP8 KV cache
 @pytest.mark.parametrize("cfg", [2, 3, 5])
 def test_fp8_small_workload_full_parity(cfg):
