@@ -188,7 +188,17 @@ def run_mixed(args):
 
     pre_ms = _timed(prefill, args.steps, args.warmup, stream, flush)
     torch.cuda.synchronize()
-    assert torch.equal(out, st.out[r0:r1]), "prefill-alone rows differ from the mixed call's"
+    # The mixed call runs the chunk in 4-wave workgroups beside the decode
+    # rows; alone it may split each q tile's keys over two groups, which
+    # changes the summation order, not the result beyond rounding.
+    alone_vs_mixed = float((out - st.out[r0:r1]).abs().max())
+    assert alone_vs_mixed <= 5e-3, f"prefill-alone rows differ from the mixed call's: {alone_vs_mixed}"
+    # k_prefill_split when every (q tile, kv head) item has a CU of its own
+    items = -(-(r1 - r0) // (128 // (w.num_q_heads // w.num_kv_heads))) * w.num_kv_heads
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    forced = os.environ.get("PKV_PREFILL_SPLIT")
+    split = forced == "1" or (forced != "0" and items <= cus)
+    chunk_kernel = "k_prefill_split" if split else "k_prefill_tile"
     flops = prefill_flops(w)
     pre_mean = float(pre_ms.mean())
     tflops = flops / (pre_mean * 1e-3) / 1e12
@@ -205,9 +215,10 @@ def run_mixed(args):
         "prefill_ms_median_p10_p90": [float(np.median(pre_ms)), float(np.percentile(pre_ms, 10)),
                                       float(np.percentile(pre_ms, 90))],
         "prefill_gflop": flops / 1e9,
+        "prefill_alone_vs_mixed_max_abs": alone_vs_mixed,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": tflops / 2500.0, "traffic": None,
-                     "kernel": "the chunk's rows alone: k_v_fp16 + k_prefill_tile",
+                     "kernel": "the chunk's rows alone: k_v_fp16 + " + chunk_kernel,
                      "algorithmic_flops_per_launch": flops},
     }
 

@@ -172,6 +172,18 @@ bool prefill_multi_query(const Plan& p, int group) {
   return !(e && std::strcmp(e, "0") == 0);
 }
 
+// Pure prefill calls on the fp16-V path whose items (q tile, kv head) each
+// get a CU of their own split every item's key tiles between two 4-wave
+// groups of one 8-wave workgroup (k_prefill_split); with more items, two
+// 4-wave workgroups share a CU (k_prefill_tile).  PKV_PREFILL_SPLIT=1 or 0
+// forces either kernel.  Returns 1, 0, or -1 for the automatic choice.
+int prefill_split_mode() {
+  const char* e = std::getenv("PKV_PREFILL_SPLIT");
+  if (e && std::strcmp(e, "1") == 0) return 1;
+  if (e && std::strcmp(e, "0") == 0) return 0;
+  return -1;
+}
+
 // Decode rows without prefill rows use the stream kernel unless
 // PKV_DECODE_SPLIT=units asks for fixed 256-token partitions plus a merge
 // launch (the path mixed batches use).
@@ -268,6 +280,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.prefill_tiles = plan.prefill_tiles;
   a.prefill_v_bf16 = prefill_reads_bf16_v(plan);
   a.prefill_mq = prefill_multi_query(plan, num_q_heads / c.hkv);
+  a.prefill_split = prefill_split_mode();
   a.prefill_seqs = plan.prefill_seqs;
   a.prefill_vblocks = plan.prefill_vblocks;
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;

@@ -60,6 +60,8 @@ struct AttnDesc {
   int64_t prefill_tiles;           // prefill q-tiles over all prefill rows
   bool prefill_v_bf16;             // prefill tiles read bf16 V from the pool (no fp16 copy)
   bool prefill_mq;                 // pure prefill, every q_len <= 32 / G: k_prefill_mq
+  int prefill_split;               // pure prefill, fp16 V: k_prefill_split 1 always, 0 never,
+                                   // -1 when every item has a CU of its own
   int prefill_seqs;                // sequences with more than one query row
   int64_t prefill_vblocks;         // blocks of the prefill sequences, each rounded up to 4
   char* ws_v;                      // fp16 V tiles of those blocks [vblock][hkv][16 * D]

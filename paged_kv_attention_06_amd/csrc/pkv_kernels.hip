@@ -1829,9 +1829,19 @@ __global__ __launch_bounds__(256) void k_v_fp16(PrefillParams p) {
 // VB: V is read as bf16 straight from the pool (through the block table,
 // like K) and P enters the P.V product as a bf16 hi + lo pair (two MFMAs);
 // otherwise V comes from the fp16 copy k_v_fp16 made in the workspace.
-template <int D, int G, bool VB>
+// SPLIT: the workgroup has 8 waves in two groups of 4 that hold the same
+// query rows; group `grp` takes one half of the item's key tiles (group 0
+// the first ceil(n / 2), group 1 the rest) into its own buffers, and at the
+// end group 1 hands its (max, sum, O) to group 0 through LDS (`xo0`, `xo1`:
+// two waves' O each; `xml`: max, sum and exponent), which merges and writes
+// the rows.  Both groups run the same number of tile iterations, so they
+// meet at every barrier.
+template <int D, int G, bool VB, bool SPLIT = false>
 __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, char* kb0,
-                                             char* kb1, char* vb0, char* vb1) {
+                                             char* kb1, char* vb0, char* vb1, int grp = 0,
+                                             char* xo0 = nullptr, char* xo1 = nullptr,
+                                             char* xml = nullptr) {
+  static_assert(!(SPLIT && VB), "the split runs the fp16-V path only");
   using S = PrefillShape<D, G>;
   static_assert(G == 1 || G == 2 || G == 4, "4 waves cover at most 4 query heads");
   constexpr int KS = S::KS, DB = S::DB;
@@ -1839,7 +1849,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);
+  const int wave = uniform((tid >> 6) & 3);
   const int kvh = work % p.hkv;
   int item = work / p.hkv;
   // The dispatcher gives workgroup w + (CU count) the CU of workgroup w.  With
@@ -1899,6 +1909,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   const int nbl = uniform((L + BS - 1) / BS);           // valid block-table entries
   // 32-key chunks this wave needs (keys up to its last row's position)
   const int nch = uniform(wlast >= wp0 ? wlast / 32 + 1 : 0);
+  // This group's key tiles [tb, te) and chunks [c_beg, c_end); niter tile
+  // iterations (the same in both groups of a split workgroup).
+  const int half_t = (nkt + 1) / 2;
+  const int tb = SPLIT && grp ? half_t : 0;
+  const int te = SPLIT && !grp ? half_t : nkt;
+  const int niter = SPLIT ? half_t : nkt;
+  const int c_beg = 2 * tb;
+  const int c_end = uniform(min(nch, 2 * te));
   const char* k_src = p.kv + (size_t)kvh * 2 * S::TILE + lane * 16;
   const char* v_src = VB ? p.kv + (size_t)(2 * kvh + 1) * S::TILE + lane * 16
                         : p.vh + ((size_t)vbase * p.hkv + kvh) * S::TILE + lane * 16;
@@ -1910,7 +1928,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   // t + 1 (its V copies start in iteration t), else the V exponents of tile t.
   const int32_t* bt_row = p.block_tables + (size_t)s * p.max_blocks;
   const int32_t* exp_row = p.vexp + (size_t)kvh * p.vblocks + vbase;
-  int meta = bt_row[min(lane & 7, nbl - 1)];  // before the loop: ids of tiles 0 and 1
+  int meta = bt_row[min(4 * tb + (lane & 7), nbl - 1)];  // before the loop: ids of tiles tb, tb + 1
   auto load_meta = [&](int t) __attribute__((always_inline)) {
     const int i = lane & 3;
     const int32_t* src = lane < 4 ? bt_row + min((t + 2) * 4 + i, nbl - 1)
@@ -2108,7 +2126,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
                       f32x16_t& s_out, const uint32_t (&hin)[8], const uint32_t (&lin)[8],
                       uint32_t (&hout)[8], uint32_t (&lout)[8]) __attribute__((always_inline)) {
     __builtin_amdgcn_sched_barrier(0);
-    if (ch >= 1 && ch <= nch) {  // P.V of chunk ch - 1
+    if (ch > c_beg && ch <= c_end) {  // P.V of chunk ch - 1
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         uint4 v[DB];
@@ -2122,12 +2140,12 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (ch + 1 < nch) {  // S^T of chunk ch + 1
+    if (ch + 1 < c_end) {  // S^T of chunk ch + 1
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qk_mfma(k_frag(kbuf, j, ks), ks, s_out);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (ch < nch) {  // softmax of chunk ch
+    if (ch < c_end) {  // softmax of chunk ch
       if (uniform(32 * ch + 31 > wp0)) sm_mask(ch, s_in);
       const float nm = sm_stats(sm_max(s_in));
 #pragma unroll
@@ -2146,7 +2164,7 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
       resc = false;
     }
     if constexpr (!VB) {
-      if (uniform(ch >= 1 && ch <= nch && (e0 != kexp || e1 != kexp))) {
+      if (uniform(ch > c_beg && ch <= c_end && (e0 != kexp || e1 != kexp))) {
         const int E = max(kexp, max(e0, e1));
         if (E > kexp) rescale_o(__builtin_ldexpf(1.f, kexp - E));
         const int ek[2] = {e0, e1};
@@ -2187,8 +2205,8 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
       ex[2] = __builtin_amdgcn_readlane(meta, 6);
       ex[3] = __builtin_amdgcn_readlane(meta, 7);
     }
-    if (t + 2 < nkt) issue_k(t + 2, knext, 0);
-    if (t + 1 < nkt) issue_v(t + 1, vnext, 4);
+    if (t + 2 < te) issue_k(t + 2, knext, 0);
+    if (t + 1 < te) issue_v(t + 1, vnext, 4);
     load_meta(t + 1);
     pre_slot(2 * t + 1, ex[0], ex[1], ph[0]);
     if constexpr (FAST)
@@ -2204,32 +2222,77 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
   using Fast = std::true_type;
   using Gen = std::false_type;
 
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);    // ids of tiles 0 and 1
-  issue_k(0, kb0, 0);
-  issue_v(0, vb0, 0);
-  if (1 < nkt) issue_k(1, kb1, 4);
-  load_meta(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);    // ids of tiles tb and tb + 1
+  if (tb < te) {
+    issue_k(tb, kb0, 0);
+    issue_v(tb, vb0, 0);
+  }
+  if (tb + 1 < te) issue_k(tb + 1, kb1, 4);
+  load_meta(tb);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  if (nch > 0) {  // S^T of chunk 0, then slot 0
+  if (c_end > c_beg) {  // S^T of chunk c_beg, then slot c_beg
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qk_mfma(k_frag(kb0, 0, ks), ks, sc[0]);
   }
-  slot_gen(0, kb0, vb0, 1, sc[0], sc[1], ph[1], pl[1], ph[0], pl[0]);
+  slot_gen(c_beg, kb0, vb0, 1, sc[0], sc[1], ph[1], pl[1], ph[0], pl[0]);
   // Leading iterations whose slots are all fast (chunk 2t + 3 exists and
   // chunk 2t + 2 ends at or before the wave's first row), then the rest.
   // Two loops rather than one with a branch per slot: the compiler would keep
-  // both sides' accumulators alive across such a branch.
-  const int n_a = max(0, (nch - 2) / 2);
-  const int n_b = wp0 >= 95 ? (wp0 - 95) / 64 + 1 : 0;
-  const int nfast = uniform(min(min(n_a, n_b), nkt));
-  for (int t = 0; t < nfast; t += 2) {
-    iter(Fast{}, t, kb1, vb0, kb0, vb1);
-    if (t + 1 < nfast) iter(Fast{}, t + 1, kb0, vb1, kb1, vb0);
+  // both sides' accumulators alive across such a branch.  Buffers alternate
+  // with the iteration's parity counted from tb.
+  const int n_a = max(0, (c_end - 2) / 2 - tb);
+  const int n_b = wp0 >= 95 ? max(0, (wp0 - 95) / 64 + 1 - tb) : 0;
+  const int nfast = uniform(min(min(n_a, n_b), te - tb));
+  for (int u = 0; u < nfast; u += 2) {
+    iter(Fast{}, tb + u, kb1, vb0, kb0, vb1);
+    if (u + 1 < nfast) iter(Fast{}, tb + u + 1, kb0, vb1, kb1, vb0);
   }
-  for (int t = nfast; t < nkt; ++t) {
-    const bool odd = t & 1;
-    iter(Gen{}, t, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1);
+  for (int u = nfast; u < niter; ++u) {
+    const bool odd = u & 1;
+    iter(Gen{}, tb + u, odd ? kb0 : kb1, odd ? vb1 : vb0, odd ? kb1 : kb0, odd ? vb0 : vb1);
+  }
+
+  if constexpr (SPLIT) {
+    // Every tile read of both groups is done; group 1's state goes through
+    // LDS (lane-major 16-byte quads: conflict-free) to group 0.
+    __syncthreads();
+    float* mo = reinterpret_cast<float*>(wave < 2 ? xo0 : xo1) + (wave & 1) * (DB * 16 * 64);
+    float* ml = reinterpret_cast<float*>(xml) + wave * 3 * 64;
+    if (grp) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4)
+          *reinterpret_cast<float4*>(mo + ((db * 4 + i4) * 64 + lane) * 4) =
+              make_float4(o[db][4 * i4], o[db][4 * i4 + 1], o[db][4 * i4 + 2], o[db][4 * i4 + 3]);
+      ml[lane] = m_run;
+      ml[64 + lane] = l_run;
+      ml[128 + lane] = __int_as_float(kexp);
+    }
+    __syncthreads();
+    if (grp) return;
+    // Both parts relative to the larger max M, o in units of 2^K with K the
+    // larger exponent.  A part that saw no key has m = -1e30 and weight 0.
+    const float m1 = ml[lane], l1 = ml[64 + lane];
+    const int k1 = uniform(__float_as_int(ml[128 + lane]));
+    const float mm = fmaxf(m_run, m1);
+    const float f0 = __builtin_amdgcn_exp2f(m_run - mm), f1 = __builtin_amdgcn_exp2f(m1 - mm);
+    l_run = l_run * f0 + l1 * f1;
+    const int kk = max(kexp, k1);
+    const float a0 = f0 * __builtin_ldexpf(1.f, kexp - kk);
+    const float a1 = f1 * __builtin_ldexpf(1.f, k1 - kk);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 b = *reinterpret_cast<const float4*>(mo + ((db * 4 + i4) * 64 + lane) * 4);
+        o[db][4 * i4] = o[db][4 * i4] * a0 + b.x * a1;
+        o[db][4 * i4 + 1] = o[db][4 * i4 + 1] * a0 + b.y * a1;
+        o[db][4 * i4 + 2] = o[db][4 * i4 + 2] * a0 + b.z * a1;
+        o[db][4 * i4 + 3] = o[db][4 * i4 + 3] * a0 + b.w * a1;
+      }
+    kexp = kk;
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -2258,6 +2321,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __align__(16) char vb0[BUF];
   __shared__ __align__(16) char vb1[BUF];
   prefill_item<D, G, VB>(p, blockIdx.x, kb0, kb1, vb0, vb1);
+}
+
+// The fp16-V tile kernel with each item's key tiles split between two groups
+// of 4 waves (see prefill_item): one 8-wave workgroup of 128 KiB LDS per CU,
+// so two waves per SIMD on every item.  For calls whose items each get a CU
+// of their own; a 4-wave workgroup alone on a CU has one wave per SIMD.
+// With more items than CUs, k_prefill_tile's two workgroups per CU overlap
+// each other's start and end, which this kernel pays per item.
+template <int D, int G>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_prefill_split(
+    PrefillParams p) {
+  constexpr int BUF = PrefillShape<D, G>::BUF;
+  static_assert(2 * BUF >= 2 * (D / 32) * 16 * 64 * 4, "two waves' O fit in one K buffer pair");
+  __shared__ __align__(16) char kb0[2][BUF];
+  __shared__ __align__(16) char kb1[2][BUF];
+  __shared__ __align__(16) char vb0[2][BUF];
+  __shared__ __align__(16) char vb1[2][BUF];
+  const int grp = uniform((int)threadIdx.x >> 8);
+  prefill_item<D, G, false, true>(p, blockIdx.x, kb0[grp], kb1[grp], vb0[grp], vb1[grp], grp,
+                                  &kb0[0][0], &kb1[0][0], &vb0[0][0]);
 }
 
 // ---- Multi-query rows: pure prefill calls whose sequences all have at most
@@ -2526,9 +2609,22 @@ static hipError_t v_fp16(const PrefillParams& p, hipStream_t stream) {
 }
 
 template <int D, bool VB>
-static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStream_t stream) {
+static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, bool split,
+                            hipStream_t stream) {
   if constexpr (!VB) {
     if (hipError_t e = v_fp16<D>(p, stream)) return e;
+    if (split) {
+      PrefillParams ps = p;
+      ps.pair_from = 0;  // one workgroup per CU: the dispatcher balances
+      const dim3 g((unsigned)grid), b(512);
+      switch (G) {
+        case 1: hipLaunchKernelGGL((k_prefill_split<D, 1>), g, b, 0, stream, ps); break;
+        case 2: hipLaunchKernelGGL((k_prefill_split<D, 2>), g, b, 0, stream, ps); break;
+        case 4: hipLaunchKernelGGL((k_prefill_split<D, 4>), g, b, 0, stream, ps); break;
+        default: return hipErrorInvalidValue;
+      }
+      return hipGetLastError();
+    }
   }
   const dim3 g((unsigned)grid), b(256);
   switch (G) {
@@ -2538,6 +2634,15 @@ static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, hipStre
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Compute units of the current device (0 if they cannot be queried).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
 }
 
 static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) {
@@ -2560,10 +2665,8 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
   // Pair heavy with light items on a CU when the prefill workgroups fill at
   // most two rounds of the CUs (more rounds are balanced by the dispatcher).
   p.pair_from = 0;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      cus > 0) {
+  const int cus = device_cus();
+  if (cus > 0) {
     const int64_t round_items = cus / c.hkv;
     if (round_items > 0 && a.prefill_tiles > round_items && a.prefill_tiles <= 2 * round_items)
       p.pair_from = (int)round_items;
@@ -2605,12 +2708,14 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
     return hipErrorInvalidValue;
   }
   const int64_t grid = a.prefill_tiles * c.hkv;
+  const int cus = device_cus();
+  const bool split = a.prefill_split > 0 || (a.prefill_split < 0 && cus > 0 && grid <= cus);
   if (a.prefill_v_bf16) {
-    if (c.head_size == 128) return prefill_g<128, true>(G, p, grid, stream);
-    if (c.head_size == 64) return prefill_g<64, true>(G, p, grid, stream);
+    if (c.head_size == 128) return prefill_g<128, true>(G, p, grid, split, stream);
+    if (c.head_size == 64) return prefill_g<64, true>(G, p, grid, split, stream);
   } else {
-    if (c.head_size == 128) return prefill_g<128, false>(G, p, grid, stream);
-    if (c.head_size == 64) return prefill_g<64, false>(G, p, grid, stream);
+    if (c.head_size == 128) return prefill_g<128, false>(G, p, grid, split, stream);
+    if (c.head_size == 64) return prefill_g<64, false>(G, p, grid, split, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -473,3 +473,42 @@ def test_prefill_v_paths(case, vpath, monkeypatch):
     st = gpu_step.run_workload(w)
     ref = scenario.run_step(w)
     _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"{case} via {vpath} V")
+
+
+# ------------------------------------- pure prefill, key tiles split over two groups
+@pytest.mark.parametrize("split", ["1", "0"])
+@pytest.mark.parametrize("G,D", [(4, 128), (2, 128), (1, 128), (4, 64), (1, 64)])
+def test_prefill_split_groups(G, D, split, monkeypatch):
+    """k_prefill_split (forced with PKV_PREFILL_SPLIT=1; chosen by itself when
+    every item has a CU of its own): two 4-wave groups share each q tile's
+    key tiles and merge (max, sum, O) in LDS.
+    Histories from 0 to 1300 tokens give odd and even key-tile counts and
+    q tiles of one key tile (group 1 idle).  V of magnitude >= 2^16 sits in
+    keys that only one group reads, so the merge meets two different
+    power-of-two exponents.  Every row against the oracle; the same batch
+    through k_prefill_tile (PKV_PREFILL_SPLIT=0)."""
+    monkeypatch.setenv("PKV_PREFILL_SPLIT", split)
+    hist = np.array([0, 37, 1300, 64, 5], np.int32)
+    ql = np.array([150, 70, 200, 2, 40], np.int32)      # longest > 64: fp16 V copy
+    streams = [np.random.default_rng(x) for x in (71 + G, 72 + D, 73, 74)]
+    w = workloads._build(0, "prefill split", "bf16", 2 * G, 2, D, D ** -0.5, hist, ql, 400, streams)
+    s2 = int(w.hist_start[2])
+    hv = w.hist_v.copy()
+    hv[s2 + 900:s2 + 906] = _times_pow2(hv[s2 + 900:s2 + 906], 22)   # keys 900..905: second half
+    w.hist_v = hv
+    nv = w.new_v.copy()
+    nv[10:13] = _times_pow2(nv[10:13], 20)                          # sequence 0, keys 10..12
+    w.new_v = nv
+    _announce(f"prefill split={split} G={G} D={D}: L={w.seq_lens.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)["out"]
+    got = st.out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got)), "non-finite output"
+    qsl = w.query_start_loc
+    for s in range(w.batch):
+        g, r = got[qsl[s]:qsl[s + 1]], ref[qsl[s]:qsl[s + 1]]
+        scale = max(float(np.abs(r).max()), 1.0)
+        max_abs = float(np.abs(g - r).max())
+        rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+        assert max_abs <= MAX_ABS_BF16 * scale, f"seq {s}: max|d| {max_abs:.3e} (scale {scale:.3e})"
+        assert rel <= REL_L2_BF16, f"seq {s}: rel L2 {rel:.3e}"
