@@ -13,7 +13,10 @@
  *  - Pointers documented "device" must point to GPU memory of the current
  *    device; "host" pointers to ordinary CPU memory.  The caller owns every
  *    buffer; the library allocates no device memory and keeps no state
- *    between calls except pkv_pool objects the caller creates and destroys.
+ *    between calls except pkv_pool objects the caller creates and destroys,
+ *    and, per device, one side stream and two events that
+ *    paged_attention_mixed creates on first use and keeps until the process
+ *    ends.
  *  - GPU work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream), asynchronously to the host.  No entry point synchronises or
  *    reads device memory from the host.
@@ -200,6 +203,10 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
  *          a PKV_FP8_E4M3 cache; rows with q_len > 1 need a bf16 cache)
  *   query_start_loc, seq_lens: device int32; h_*: equal host copies
  *   num_tokens == query_start_loc[num_seqs]
+ * A call with both kinds of rows forks the prefill rows onto the library's
+ * side stream of the current device (an event recorded on `stream`) and
+ * joins it back (`stream` waits for an event recorded on the side stream),
+ * so the work is still ordered by `stream` and can be captured from it.
  * Host-checked: q_len_s <= seq_lens[s] <= max_blocks_per_seq * 16. */
 int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
                           int32_t num_q_heads, const int32_t* query_start_loc,

@@ -184,6 +184,14 @@ int prefill_split_mode() {
   return -1;
 }
 
+// Mixed calls run the prefill tiles on a side stream beside the stream
+// decode of their decode rows (one wave per SIMD each), unless
+// PKV_MIXED=fused asks for the single k_mixed launch with fixed partitions.
+bool mixed_concurrent_enabled() {
+  const char* e = std::getenv("PKV_MIXED");
+  return !(e && std::strcmp(e, "fused") == 0);
+}
+
 // Decode rows without prefill rows use the stream kernel unless
 // PKV_DECODE_SPLIT=units asks for fixed 256-token partitions plus a merge
 // launch (the path mixed batches use).
@@ -192,34 +200,35 @@ bool stream_decode_enabled() {
   return !(e && std::strcmp(e, "units") == 0);
 }
 
-// Workspace layout: header | decode partials acc [units][hq][D], (m, l)
-// [units][hq][2] | (256-aligned) fp16 V tiles [vblocks][hkv][16 D] | their
-// exponents [hkv][vblocks].  A call without prefill rows may instead run the
-// stream kernel: header | partials acc [2 waves][G][D], (m, l) [2 waves][G][2]
-// | (256-aligned) counters [num_seqs][hkv] (8 bytes each); it is given the
-// larger of the two sizes.
+// Workspace layout: header | decode partials | (256-aligned) fp16 V tiles
+// [vblocks][hkv][16 D] | their exponents [hkv][vblocks].  The decode
+// partials region is the larger of the two decode paths' needs: fixed
+// partitions, acc [units][hq][D] then (m, l) [units][hq][2]; or the stream
+// kernel, acc [2 waves][G][D], (m, l) [2 waves][G][2], then (256-aligned)
+// counters [num_seqs][hkv] (8 bytes each).
 struct WsLayout {
   size_t v_off, exp_off, total;
   size_t st_ml_off, st_ctr_off;  // stream layout (offsets from the start)
 };
 WsLayout ws_layout(const Plan& p, int hq, int hkv, int D) {
   WsLayout w{0, 0, 0, 0, 0};
-  if (p.decode_units > 0 && p.prefill_tiles == 0) {
+  size_t dec_end = pkv::kWorkspaceHeader;
+  if (p.decode_units > 0) {
     const int G = hq / hkv;
     const size_t wc = (size_t)stream_wave_cap(p, hkv);
     w.st_ml_off = pkv::kWorkspaceHeader + 2 * wc * G * D * sizeof(float);
     w.st_ctr_off = (w.st_ml_off + 2 * wc * G * 2 * sizeof(float) + 255) / 256 * 256;
     const size_t st_total = w.st_ctr_off + (size_t)p.num_seqs * hkv * 8;
     const size_t units = pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
-    w.total = st_total > units ? st_total : units;
+    dec_end = st_total > units ? st_total : units;
+  }
+  if (p.prefill_vblocks == 0) {
+    w.total = p.decode_units > 0 ? dec_end : 0;
     return w;
   }
-  if (p.decode_units == 0 && p.prefill_vblocks == 0) return w;
-  const size_t dec = (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
-  w.v_off = (pkv::kWorkspaceHeader + dec + 255) / 256 * 256;
+  w.v_off = (dec_end + 255) / 256 * 256;
   w.exp_off = w.v_off + (size_t)p.prefill_vblocks * hkv * pkv::kBlockSize * D * 2;
-  w.total = p.prefill_vblocks ? w.exp_off + (size_t)p.prefill_vblocks * hkv * sizeof(int32_t)
-                              : pkv::kWorkspaceHeader + dec;
+  w.total = w.exp_off + (size_t)p.prefill_vblocks * hkv * sizeof(int32_t);
   return w;
 }
 
@@ -286,9 +295,14 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   a.stream_waves = 0;
-  if (plan.prefill_tiles == 0 && plan.decode_units > 0 && (stream_decode_enabled() || c.fp8)) {
+  const bool mixed_call = plan.prefill_tiles > 0 && plan.decode_units > 0;
+  if (plan.decode_units > 0 && (stream_decode_enabled() || c.fp8) &&
+      (!mixed_call || mixed_concurrent_enabled())) {
     const int G = num_q_heads / c.hkv;
-    const int slots = pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
+    // Beside prefill tiles the decode keeps one wave per SIMD: a SIMD then
+    // holds one prefill wave and one decode wave.
+    const int slots = mixed_call ? 4 * pkv::device_cus()
+                                 : pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
     int64_t waves = stream_wave_cap(plan, c.hkv);
     if (slots > 0 && slots < waves) waves = slots;
     if (const char* e = std::getenv("PKV_STREAM_WAVES")) {  // tuning: cap the waves

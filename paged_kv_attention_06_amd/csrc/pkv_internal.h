@@ -88,14 +88,19 @@ hipError_t launch_block_swap(const CacheDesc& c, char* host_dev_ptr, const int64
 hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 // Prefill rows of a mixed batch (q_len > 1) when it has no decode rows: MFMA tiles.
 hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
-// A batch with both kinds of rows: one launch in which prefill tiles and
-// decode units share the GPU, then the merge of split decode rows.
+// A batch with both kinds of rows.  With stream_waves > 0: the prefill
+// tiles on the library's side stream (one workgroup per CU) beside the
+// stream decode of the decode rows on `stream`, joined back into `stream`.
+// Otherwise one launch in which prefill tiles and fixed decode partitions
+// share the GPU, then the merge of split decode rows.
 hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 
 bool supported_group(int g);
 // Waves of the stream decode kernel the current device holds at once (0 if
 // it cannot be queried).
 int decode_stream_slots(int dtype_bytes, int D, int G);
+// Compute units of the current device (0 if they cannot be queried).
+int device_cus();
 // Group sizes the mixed path's prefill rows support (bf16 caches only).
 inline bool prefill_supported(int g, int dtype_bytes) {
   return dtype_bytes == 2 && (g == 1 || g == 2 || g == 4);

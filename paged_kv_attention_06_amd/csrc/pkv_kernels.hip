@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdint.h>
 
 #include "pkv_internal.h"
@@ -1677,6 +1678,7 @@ struct PrefillParams {
   int64_t vblocks;   // blocks of all prefill sequences, each rounded up to 4
   int items;         // prefill q tiles over all sequences (workgroups / hkv)
   int pair_from;     // > 0: item slots >= pair_from run the lightest items in reverse
+  int prio;          // 1: the tile waves raise their issue priority (beside decode waves)
 };
 
 template <int D, int G>
@@ -2320,6 +2322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __align__(16) char kb1[BUF];
   __shared__ __align__(16) char vb0[BUF];
   __shared__ __align__(16) char vb1[BUF];
+  if (p.prio) __builtin_amdgcn_s_setprio(3);
   prefill_item<D, G, VB>(p, blockIdx.x, kb0, kb1, vb0, vb1);
 }
 
@@ -2608,11 +2611,14 @@ static hipError_t v_fp16(const PrefillParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// `lds_pad`: extra LDS bytes per 4-wave workgroup (limits how many share a CU).
 template <int D, bool VB>
 static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, bool split,
-                            hipStream_t stream) {
+                            hipStream_t stream, size_t lds_pad = 0, bool v_done = false) {
   if constexpr (!VB) {
-    if (hipError_t e = v_fp16<D>(p, stream)) return e;
+    if (!v_done) {
+      if (hipError_t e = v_fp16<D>(p, stream)) return e;
+    }
     if (split) {
       PrefillParams ps = p;
       ps.pair_from = 0;  // one workgroup per CU: the dispatcher balances
@@ -2627,17 +2633,17 @@ static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, bool sp
     }
   }
   const dim3 g((unsigned)grid), b(256);
+  const unsigned pad = (unsigned)lds_pad;
   switch (G) {
-    case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1, VB>), g, b, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2, VB>), g, b, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((k_prefill_tile<D, 4, VB>), g, b, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((k_prefill_tile<D, 1, VB>), g, b, pad, stream, p); break;
+    case 2: hipLaunchKernelGGL((k_prefill_tile<D, 2, VB>), g, b, pad, stream, p); break;
+    case 4: hipLaunchKernelGGL((k_prefill_tile<D, 4, VB>), g, b, pad, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// Compute units of the current device (0 if they cannot be queried).
-static int device_cus() {
+int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -2665,6 +2671,7 @@ static PrefillParams make_prefill_params(const CacheDesc& c, const AttnDesc& a) 
   // Pair heavy with light items on a CU when the prefill workgroups fill at
   // most two rounds of the CUs (more rounds are balanced by the dispatcher).
   p.pair_from = 0;
+  p.prio = 0;
   const int cus = device_cus();
   if (cus > 0) {
     const int64_t round_items = cus / c.hkv;
@@ -2730,8 +2737,79 @@ static hipError_t mixed_t(const MixedParams& m, int64_t grid, int num_seqs, int 
   return hipGetLastError();
 }
 
+// The library's side stream of a device, with the events that fork work
+// onto it from a caller's stream and join it back.  Created on first use
+// (default priority, non-blocking) and kept until the process ends.  The
+// mutex keeps one call's record / wait pairs together when host threads
+// call at once.
+struct SideStream {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+constexpr int kMaxDevices = 64;
+static SideStream g_side[kMaxDevices];
+
+static SideStream* side_stream(hipError_t* err) {
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  SideStream& ss = g_side[dev];
+  std::call_once(ss.once, [&ss]() {
+    ss.err = hipStreamCreateWithFlags(&ss.side, hipStreamNonBlocking);
+    if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming);
+    if (ss.err == hipSuccess) ss.err = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming);
+  });
+  *err = ss.err;
+  return ss.err == hipSuccess ? &ss : nullptr;
+}
+
+// Prefill tiles (HBM-light, MFMA-bound) and decode rows (HBM-bound) of one
+// mixed call side by side.  The fp16 copy of V is made first, alone.  Then
+// the tile kernel gets ~81 KiB of LDS per workgroup, so one shares a CU (one
+// wave per SIMD, ~200 VGPRs); the stream decode runs one wave per SIMD
+// (~220 VGPRs), and both fit a SIMD's 512.  The tile waves take the higher
+// issue priority: the decode waves mostly wait for memory.
+static hipError_t mixed_concurrent(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  SideStream* ss = side_stream(&e);
+  if (!ss) return e;
+  PrefillParams p = make_prefill_params(c, a);
+  p.pair_from = 0;  // one workgroup per CU: heaviest first, the dispatcher balances
+  p.prio = 1;
+  const int G = a.hq / c.hkv;
+  const int64_t grid = a.prefill_tiles * c.hkv;
+  constexpr size_t kCuLds = 160 * 1024;
+  if (c.head_size == 128)
+    e = v_fp16<128>(p, stream);
+  else if (c.head_size == 64)
+    e = v_fp16<64>(p, stream);
+  else
+    return hipErrorInvalidValue;
+  if (e) return e;
+  std::lock_guard<std::mutex> lock(ss->mu);
+  if ((e = hipEventRecord(ss->fork, stream))) return e;
+  if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0))) return e;
+  if (c.head_size == 128)
+    e = prefill_g<128, false>(G, p, grid, false, ss->side,
+                              kCuLds / 2 + 1024 - PrefillShape<128, 4>::BUF * 4, true);
+  else
+    e = prefill_g<64, false>(G, p, grid, false, ss->side,
+                             kCuLds / 2 + 1024 - PrefillShape<64, 4>::BUF * 4, true);
+  if (e) return e;
+  if ((e = launch_decode_stream(c, a, stream))) return e;
+  if ((e = hipEventRecord(ss->join, ss->side))) return e;
+  return hipStreamWaitEvent(stream, ss->join, 0);
+}
+
 hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   if (c.dtype_bytes != 2) return hipErrorInvalidValue;
+  if (a.stream_waves > 0) return mixed_concurrent(c, a, stream);
   MixedParams m;
   m.pp = make_prefill_params(c, a);
   m.dp = make_decode_params(c, a);

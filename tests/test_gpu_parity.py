@@ -250,6 +250,36 @@ def test_fixed_partition_decode_path(cfg, monkeypatch):
     _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"units split {w.name}")
 
 
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_fused_mixed_path(size, monkeypatch):
+    """Mixed calls run the prefill tiles on the library's side stream beside
+    the stream decode; PKV_MIXED=fused runs the single k_mixed launch (fixed
+    decode partitions + merge launch) instead.  Both against the oracle, and
+    the two paths against each other on the same step."""
+    w = workloads.small(4) if size == "small" else workloads.make(4)
+    _announce(f"fused mixed path, {size} {w.name}")
+    st = gpu_step.run_workload(w)
+    concurrent = st.out.cpu().numpy()
+    monkeypatch.setenv("PKV_MIXED", "fused")
+    st.out.fill_(0)
+    st.attend()
+    torch.cuda.synchronize()
+    fused = st.out.cpu().numpy()
+    if size == "small":
+        ref = scenario.run_step(w)["out"]
+        _check_attention(fused, ref, "bf16", "fused mixed")
+        _check_attention(concurrent, ref, "bf16", "concurrent mixed")
+    else:
+        seqs = _sample_seqs(w)
+        for s in seqs:
+            rows = slice(int(w.query_start_loc[s]), int(w.query_start_loc[s + 1]))
+            if rows.stop - rows.start > 1:
+                continue  # the chunk's rows: checked against the oracle elsewhere
+            ref = scenario.sequence_attention(w, s)
+            _check_attention(fused[rows], ref, "bf16", f"fused row {s}")
+    assert float(np.abs(fused - concurrent).max()) <= MAX_ABS_BF16, "fused and concurrent paths differ"
+
+
 def test_workspace_reused_with_new_queries():
     """Two calls in a row on one workspace with different queries: the second
     call's merged rows must not see partials or counters left by the first."""

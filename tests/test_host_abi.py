@@ -196,7 +196,14 @@ def test_workspace_sizing():
     # up to whole 64-key tiles, for every kv head, and one int32 exponent each
     vblocks = 4 * -(-8192 // 64)
     prefill = vblocks * 8 * (16 * 128 * 2 + 4)
+    # the decode rows' region fits either decode path: fixed partitions, or
+    # the stream kernel sized by the decode rows alone (rows 0..2)
     dec = header + 4 * 32 * 130 * 4
+    cost_d = 8 * sum(-(-int(x) // 32) + 1 for x in lens[:3])
+    waves_d = min(4096, -(-cost_d // 8))
+    ml_end_d = header + 2 * waves_d * 4 * 128 * 4 + 2 * waves_d * 4 * 2 * 4
+    stream_d = -(-ml_end_d // 256) * 256 + 5 * 8 * 8
+    dec = max(dec, stream_d)
     assert P.pkv_attention_workspace_bytes(cache, 32, lens, qsl) == -(-dec // 256) * 256 + prefill
     only_prefill = np.array([0, 1000], np.int32)
     assert P.pkv_attention_workspace_bytes(cache, 32, lens[4:], only_prefill) == header + prefill
