@@ -145,9 +145,10 @@ int64_t stream_wave_cap(const Plan& p, int hkv) {
 
 // Epochs of stream-decode counters start at a value that differs between
 // runs, so counters left in a reused buffer by another process are stale.
+// They are odd (the kernel parks finished counters at 0) and step by 2.
 unsigned first_epoch() {
   const auto t = std::chrono::steady_clock::now().time_since_epoch().count();
-  return (unsigned)t ^ (unsigned)((unsigned long long)t >> 32) ^ 0x9E3779B9u;
+  return ((unsigned)t ^ (unsigned)((unsigned long long)t >> 32) ^ 0x9E3779B9u) | 1u;
 }
 
 // Prefill tiles of calls whose prefill rows are all short (at most 64 query
@@ -314,7 +315,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
       a.stream_total = stream_total(plan, c.hkv);
       a.stream_waves = (int)waves;
       a.stream_c0 = pkv::kStreamSetupCost;
-      a.stream_epoch = epoch.fetch_add(1, std::memory_order_relaxed);
+      a.stream_epoch = epoch.fetch_add(2, std::memory_order_relaxed);
       a.stream_acc = reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader);
       a.stream_ml = reinterpret_cast<float*>(ws + wl.st_ml_off);
       a.stream_counters = reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off);

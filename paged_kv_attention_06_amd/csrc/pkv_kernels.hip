@@ -848,7 +848,10 @@ __global__ __launch_bounds__(256) void k_decode_merge(DecodeParams p) {
 // counter, and the last one merges the partials into the output row, so no
 // second launch is needed.  Counters carry the call's epoch in their upper
 // half: a counter whose epoch differs is stale and counts as zero, so the
-// workspace needs no clearing between calls.
+// workspace needs no clearing between calls.  The merging wave puts its
+// counter back to 0 (epochs are odd, so 0 is never current): a graph that
+// replays a captured call, epoch and all, then starts every replay from
+// stale counters too.
 // ---------------------------------------------------------------------------
 // Partials travel between waves that may sit on different XCDs, whose L2
 // caches are not coherent with each other.  They are written and read with
@@ -1465,10 +1468,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   }
   const unsigned cnt0 = (unsigned)__builtin_amdgcn_readlane((int)cnt, 0);
   const unsigned cnt1 = (unsigned)__builtin_amdgcn_readlane((int)cnt, 1);
-  if (cnt0 == (unsigned)(pend0.wB - pend0.wA + 1))
+  const bool last0 = cnt0 == (unsigned)(pend0.wB - pend0.wA + 1);
+  const bool last1 = npend > 1 && cnt1 == (unsigned)(pend1.wB - pend1.wA + 1);
+  // Every contributor has counted itself in: no wave of this call touches
+  // these counters again.
+  if ((lane == 0 && last0) || (lane == 1 && last1))
+    __hip_atomic_store(sp.counters + (lane == 0 ? pend0.ctr : pend1.ctr), 0ULL, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (last0)
     stream_merge<ES, D, G>(sp, pend0.wA, pend0.wB,
                            p.out + ((size_t)pend0.row * hq + (size_t)pend0.h * G) * D);
-  if (npend > 1 && cnt1 == (unsigned)(pend1.wB - pend1.wA + 1))
+  if (last1)
     stream_merge<ES, D, G>(sp, pend1.wA, pend1.wB,
                            p.out + ((size_t)pend1.row * hq + (size_t)pend1.h * G) * D);
 }

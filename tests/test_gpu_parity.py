@@ -542,3 +542,45 @@ def test_prefill_split_groups(G, D, split, monkeypatch):
         rel = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
         assert max_abs <= MAX_ABS_BF16 * scale, f"seq {s}: max|d| {max_abs:.3e} (scale {scale:.3e})"
         assert rel <= REL_L2_BF16, f"seq {s}: rel L2 {rel:.3e}"
+
+
+# ------------------------------------------------------------ graph replay
+@pytest.mark.parametrize("kind", ["decode", "mixed"])
+def test_graph_replay_matches_eager(kind):
+    """An attention call captured in a graph and replayed four times, with
+    new queries copied in before each replay and eager calls in between:
+    every replay equals the eager call on the same queries bit for bit.  The
+    stream decode's split rows are merged by their last contributor through
+    counters in the workspace; a replay reuses the captured call's epoch, so
+    this fails if a finished counter is not put back.  The mixed call also
+    forks its prefill tiles onto the library's side stream inside the
+    capture."""
+    w = workloads.make(3, batch=64) if kind == "decode" else workloads.small(4)
+    _announce(f"graph replay, {kind}: B={w.batch} T={w.num_tokens}")
+    st = gpu_step.run_workload(w)                     # eager first: side stream, warm-up
+    rng = np.random.default_rng(5)
+    qs = [torch.from_numpy((rng.standard_normal(tuple(st.q.shape)).astype(np.float32)
+                            .view(np.uint32) >> 16).astype(np.uint16).view(np.int16)).cuda()
+          for _ in range(4)]
+    assert qs[0].dtype == st.q.dtype
+    eager = []
+    for q in qs:
+        st.q.copy_(q)
+        st.attend()
+        torch.cuda.synchronize()
+        eager.append(st.out.clone())
+    assert not torch.equal(eager[0], eager[1])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.attend()
+    torch.cuda.synchronize()
+    for i, q in enumerate(qs):
+        st.q.copy_(q)
+        st.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, eager[i]), f"replay {i} differs from the eager call"
+        st.q.copy_(qs[(i + 1) % 4])                   # an eager call between replays
+        st.attend()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out, eager[(i + 1) % 4]), f"eager call after replay {i} differs"
