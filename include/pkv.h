@@ -206,7 +206,9 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
  * A call with both kinds of rows forks the prefill rows onto the library's
  * side stream of the current device (an event recorded on `stream`) and
  * joins it back (`stream` waits for an event recorded on the side stream),
- * so the work is still ordered by `stream` and can be captured from it.
+ * so the work is still ordered by `stream` and can be captured from it.  The
+ * side stream and its events are created by the first such call on a device;
+ * make that call outside graph capture.
  * Host-checked: q_len_s <= seq_lens[s] <= max_blocks_per_seq * 16. */
 int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
                           int32_t num_q_heads, const int32_t* query_start_loc,

@@ -2805,16 +2805,18 @@ static hipError_t mixed_concurrent(const CacheDesc& c, const AttnDesc& a, hipStr
   std::lock_guard<std::mutex> lock(ss->mu);
   if ((e = hipEventRecord(ss->fork, stream))) return e;
   if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0))) return e;
+  // Once forked, the side stream is always joined back, also when a launch
+  // failed, so nothing of this call runs unordered with the caller's stream.
   if (c.head_size == 128)
     e = prefill_g<128, false>(G, p, grid, false, ss->side,
                               kCuLds / 2 + 1024 - PrefillShape<128, 4>::BUF * 4, true);
   else
     e = prefill_g<64, false>(G, p, grid, false, ss->side,
                              kCuLds / 2 + 1024 - PrefillShape<64, 4>::BUF * 4, true);
-  if (e) return e;
-  if ((e = launch_decode_stream(c, a, stream))) return e;
-  if ((e = hipEventRecord(ss->join, ss->side))) return e;
-  return hipStreamWaitEvent(stream, ss->join, 0);
+  const hipError_t e_dec = e ? hipSuccess : launch_decode_stream(c, a, stream);
+  hipError_t e_join = hipEventRecord(ss->join, ss->side);
+  if (e_join == hipSuccess) e_join = hipStreamWaitEvent(stream, ss->join, 0);
+  return e ? e : e_dec ? e_dec : e_join;
 }
 
 hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
