@@ -223,6 +223,61 @@ def run_mixed(args):
     }
 
 
+def run_prefill(args):
+    """One prefill chunk alone in the 8B GQA shape (32 q / 8 kv heads, head
+    128, bf16): `--chunk-rows` causal query rows on `--cached` cached
+    tokens, through paged_attention_mixed."""
+    import torch
+
+    import workloads
+    from paged_kv_attention_06_amd import step as gpu_step
+
+    rows, cached = args.chunk_rows, args.cached
+    if rows < 2 or cached < 0:
+        raise SystemExit("--chunk-rows must be >= 2 and --cached >= 0")
+    streams = [np.random.default_rng(x)
+               for x in np.random.SeedSequence(4_000 + rows + 7 * cached).spawn(4)]
+    blocks = -(-(cached + rows) // 16)
+    w = workloads._build(4, f"8B GQA prefill chunk: {rows} rows on {cached} cached tokens", "bf16",
+                         32, 8, 128, 128 ** -0.5, np.array([cached], np.int32),
+                         np.array([rows], np.int32), blocks + blocks // 4 + 8, streams)
+    st = gpu_step.PagedStep(w, "cuda")
+    st.build_history()
+    st.prepare_step()
+    st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    flush = make_flush(args.flush_mb)
+    ms = _timed(st.attend, args.steps, args.warmup, stream, flush)
+    flops = prefill_flops(w)
+    mean = float(ms.mean())
+    tflops = flops / (mean * 1e-3) / 1e12
+    # the kernel the library picks for this call (see the tuning switches)
+    items = -(-rows // 32) * w.num_kv_heads
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    forced = os.environ.get("PKV_PREFILL_SPLIT")
+    if rows <= 8 and os.environ.get("PKV_PREFILL_MQ") != "0":
+        kernel = "k_prefill_mq"
+    elif rows <= 64 and os.environ.get("PKV_PREFILL_V") != "fp16":
+        kernel = "k_prefill_tile (bf16 V from the pool)"
+    else:
+        split = forced == "1" or (forced != "0" and items <= cus)
+        kernel = "k_v_fp16 + " + ("k_prefill_split" if split else "k_prefill_tile")
+    return {
+        "metric": "prefill chunk alone: MFMA TFLOP/s of the unmasked (query, key) pairs",
+        "value": tflops, "unit": "TFLOP/s", "higher_is_better": True,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mean,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "flush_mb_read_before_each_step": args.flush_mb},
+        "attention_ms_median": float(np.median(ms)),
+        "items_q_tile_x_kv_head": items,
+        "gflop": flops / 1e9,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tflops / 2500.0, "traffic": None, "kernel": kernel,
+                     "algorithmic_flops_per_launch": flops},
+    }
+
+
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 
 
@@ -321,7 +376,8 @@ def main() -> None:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["decode", "mixed", "decode-fp8", "verify", "swap",
-                                           "prefix-cache", "decode-7b", "decode-13b", "tiny"],
+                                           "prefix-cache", "decode-7b", "decode-13b", "tiny",
+                                           "prefill"],
                     default="decode",
                     help="decode: the headline 8B GQA batch-256 step; mixed: the chunked "
                          "prefill step; decode-fp8: the headline step on an FP8 E4M3 KV "
@@ -329,6 +385,10 @@ def main() -> None:
                          "sequence (speculative decoding); all but decode are reported "
                          "separately")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk-rows", type=int, default=512,
+                    help="prefill workload: query rows of the chunk")
+    ap.add_argument("--cached", type=int, default=1048,
+                    help="prefill workload: cached tokens before the chunk")
     ap.add_argument("--flush-mb", type=int, default=1024,
                     help="read this many MiB of scratch before every timed step, so that no "
                          "step reuses the last one's cached data (0 = back to back)")
@@ -356,6 +416,9 @@ def main() -> None:
         return
     if args.workload == "swap":
         print(json.dumps(run_swap(args)), flush=True)
+        return
+    if args.workload == "prefill":
+        print(json.dumps(run_prefill(args)), flush=True)
         return
 
     fp8 = args.workload == "decode-fp8"
