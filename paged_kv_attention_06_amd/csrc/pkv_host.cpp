@@ -193,9 +193,9 @@ bool mixed_concurrent_enabled() {
   return !(e && std::strcmp(e, "fused") == 0);
 }
 
-// Decode rows without prefill rows use the stream kernel unless
-// PKV_DECODE_SPLIT=units asks for fixed 256-token partitions plus a merge
-// launch (the path mixed batches use).
+// Decode rows use the stream kernel unless PKV_DECODE_SPLIT=units asks for
+// fixed 256-token partitions plus a merge launch (in a mixed call: the
+// single k_mixed launch, as with PKV_MIXED=fused).
 bool stream_decode_enabled() {
   const char* e = std::getenv("PKV_DECODE_SPLIT");
   return !(e && std::strcmp(e, "units") == 0);

@@ -2586,10 +2586,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
-// One launch for a mixed batch: workgroups [0, n_prefill) run prefill tiles
-// (compute-bound, MFMA) and the rest run four decode items each, one per
-// wave (bandwidth-bound), so both kinds of work share the CUs instead of
-// running back to back.
+// One launch for a mixed batch (PKV_MIXED=fused): workgroups [0, n_prefill)
+// run prefill tiles (compute-bound, MFMA) and the rest run four decode items
+// each, one per wave (bandwidth-bound).  Every workgroup holds the prefill
+// tiles' 64 KiB of LDS, so the decode workgroups mostly follow the prefill
+// ones; the default mixed path runs the two kinds of work side by side on
+// two streams instead (mixed_concurrent).
 struct MixedParams {
   PrefillParams pp;
   DecodeParams dp;
