@@ -1780,6 +1780,7 @@ __device__ __forceinline__ float bf16x2_absmax(uint32_t w) {
 // by 2^-e with e the smallest exponent that brings every |v| below 2^16.
 template <int D>
 __global__ __launch_bounds__(256) void k_v_fp16(PrefillParams p) {
+  if (p.prio) __builtin_amdgcn_s_setprio(3);
   constexpr int TILE = BS * D * 2;
   constexpr int NG = TILE / 16 / 64;  // granules per lane
   const int lane = threadIdx.x & 63;
@@ -2626,11 +2627,9 @@ static hipError_t v_fp16(const PrefillParams& p, hipStream_t stream) {
 // `lds_pad`: extra LDS bytes per 4-wave workgroup (limits how many share a CU).
 template <int D, bool VB>
 static hipError_t prefill_g(int G, const PrefillParams& p, int64_t grid, bool split,
-                            hipStream_t stream, size_t lds_pad = 0, bool v_done = false) {
+                            hipStream_t stream, size_t lds_pad = 0) {
   if constexpr (!VB) {
-    if (!v_done) {
-      if (hipError_t e = v_fp16<D>(p, stream)) return e;
-    }
+    if (hipError_t e = v_fp16<D>(p, stream)) return e;
     if (split) {
       PrefillParams ps = p;
       ps.pair_from = 0;  // one workgroup per CU: the dispatcher balances
@@ -2782,11 +2781,12 @@ static SideStream* side_stream(hipError_t* err) {
 }
 
 // Prefill tiles (HBM-light, MFMA-bound) and decode rows (HBM-bound) of one
-// mixed call side by side.  The fp16 copy of V is made first, alone.  Then
-// the tile kernel gets ~81 KiB of LDS per workgroup, so one shares a CU (one
-// wave per SIMD, ~200 VGPRs); the stream decode runs one wave per SIMD
-// (~220 VGPRs), and both fit a SIMD's 512.  The tile waves take the higher
-// issue priority: the decode waves mostly wait for memory.
+// mixed call side by side: the fp16 copy of V and then the tiles on the
+// side stream, the stream decode on the caller's.  The tile kernel gets ~81
+// KiB of LDS per workgroup, so one shares a CU (one wave per SIMD, ~200
+// VGPRs); the stream decode runs one wave per SIMD (~220 VGPRs), and both
+// fit a SIMD's 512.  The prefill waves take the higher issue priority: the
+// decode waves mostly wait for memory.
 static hipError_t mixed_concurrent(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   hipError_t e = hipSuccess;
   SideStream* ss = side_stream(&e);
@@ -2797,13 +2797,7 @@ static hipError_t mixed_concurrent(const CacheDesc& c, const AttnDesc& a, hipStr
   const int G = a.hq / c.hkv;
   const int64_t grid = a.prefill_tiles * c.hkv;
   constexpr size_t kCuLds = 160 * 1024;
-  if (c.head_size == 128)
-    e = v_fp16<128>(p, stream);
-  else if (c.head_size == 64)
-    e = v_fp16<64>(p, stream);
-  else
-    return hipErrorInvalidValue;
-  if (e) return e;
+  if (c.head_size != 128 && c.head_size != 64) return hipErrorInvalidValue;
   std::lock_guard<std::mutex> lock(ss->mu);
   if ((e = hipEventRecord(ss->fork, stream))) return e;
   if ((e = hipStreamWaitEvent(ss->side, ss->fork, 0))) return e;
@@ -2811,10 +2805,10 @@ static hipError_t mixed_concurrent(const CacheDesc& c, const AttnDesc& a, hipStr
   // failed, so nothing of this call runs unordered with the caller's stream.
   if (c.head_size == 128)
     e = prefill_g<128, false>(G, p, grid, false, ss->side,
-                              kCuLds / 2 + 1024 - PrefillShape<128, 4>::BUF * 4, true);
+                              kCuLds / 2 + 1024 - PrefillShape<128, 4>::BUF * 4);
   else
     e = prefill_g<64, false>(G, p, grid, false, ss->side,
-                             kCuLds / 2 + 1024 - PrefillShape<64, 4>::BUF * 4, true);
+                             kCuLds / 2 + 1024 - PrefillShape<64, 4>::BUF * 4);
   const hipError_t e_dec = e ? hipSuccess : launch_decode_stream(c, a, stream);
   hipError_t e_join = hipEventRecord(ss->join, ss->side);
   if (e_join == hipSuccess) e_join = hipStreamWaitEvent(stream, ss->join, 0);
