@@ -584,3 +584,23 @@ def test_graph_replay_matches_eager(kind):
         st.attend()
         torch.cuda.synchronize()
         assert torch.equal(st.out, eager[(i + 1) % 4]), f"eager call after replay {i} differs"
+
+
+@pytest.mark.parametrize("mode", ["concurrent", "fused"])
+@pytest.mark.parametrize("G,D", [(4, 128), (2, 128), (1, 128), (4, 64), (2, 64), (1, 64)])
+def test_mixed_paths_group_and_head_sizes(G, D, mode, monkeypatch):
+    """Mixed calls for every supported query-head group and head size: the
+    side-stream path (tiles with their LDS request beside the stream decode)
+    and the single fused launch (PKV_MIXED=fused).  Decode rows of assorted
+    lengths (one of length 1), a 130-row chunk starting mid-block and a short
+    multi-row sequence; every row against the oracle."""
+    if mode == "fused":
+        monkeypatch.setenv("PKV_MIXED", "fused")
+    hist = np.array([300, 0, 17, 1000, 37, 90], np.int32)
+    ql = np.array([1, 1, 1, 1, 130, 5], np.int32)
+    streams = [np.random.default_rng(x) for x in (81 + G, 82 + D, 83, 84)]
+    w = workloads._build(4, "mixed shapes", "bf16", 2 * G, 2, D, D ** -0.5, hist, ql, 300, streams)
+    _announce(f"mixed {mode} G={G} D={D}: L={w.seq_lens.tolist()} q_len={w.q_len.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"mixed {mode} G={G} D={D}")
