@@ -296,7 +296,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.ws_v = plan.prefill_vblocks ? ws + wl.v_off : nullptr;
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   a.stream_waves = 0;
-  a.stream_flip = false;
+  a.stream_rounds = 0;
   const bool mixed_call = plan.prefill_tiles > 0 && plan.decode_units > 0;
   if (plan.decode_units > 0 && (stream_decode_enabled() || c.fp8) &&
       (!mixed_call || mixed_concurrent_enabled())) {
@@ -317,7 +317,11 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
       a.stream_waves = (int)waves;
       a.stream_c0 = pkv::kStreamSetupCost;
       a.stream_epoch = epoch.fetch_add(2, std::memory_order_relaxed);
-      a.stream_flip = !mixed_call;  // beside prefill tiles there is one decode wave per SIMD
+      // waves per SIMD (rounds of dispatch), which rotate their priority;
+      // beside prefill tiles there is one decode wave per SIMD: off
+      const int simds = 4 * pkv::device_cus();
+      const int64_t rounds = simds > 0 ? (waves + simds - 1) / simds : 0;
+      a.stream_rounds = (!mixed_call && rounds > 1) ? (int)(rounds < 4 ? rounds : 4) : 0;
       a.stream_acc = reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader);
       a.stream_ml = reinterpret_cast<float*>(ws + wl.st_ml_off);
       a.stream_counters = reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off);

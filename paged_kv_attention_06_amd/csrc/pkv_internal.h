@@ -71,7 +71,7 @@ struct AttnDesc {
   int stream_waves;                // ranges / waves of the launch
   int stream_c0;                   // setup charge per item
   unsigned stream_epoch;           // distinct per call
-  bool stream_flip;                // the two waves of a SIMD alternate their issue priority
+  int stream_rounds;               // > 1: waves per SIMD, which rotate their issue priority
   unsigned long long* stream_counters;  // [num_seqs][hkv]
   float* stream_acc;               // [2 * waves][G][D]
   float* stream_ml;                // [2 * waves][G][2]

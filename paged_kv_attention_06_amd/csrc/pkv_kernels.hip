@@ -876,7 +876,7 @@ struct StreamParams {
   int waves;                     // ranges = grid size
   int c0;                        // setup charge per item, in steps
   unsigned epoch;                // distinct per call
-  int flip;                      // 1: the waves of a SIMD alternate their issue priority
+  int rounds;                    // > 1: waves per SIMD, which rotate their issue priority
   unsigned long long* counters;  // [num_seqs][hkv]
   float* part_acc;               // [2 * waves][G][D]
   float* part_ml;                // [2 * waves][G][2]
@@ -1435,25 +1435,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     return c2;
   };
 
-  // Two waves share each SIMD (waves w and w + W / 2 in dispatch order), and
-  // the issue arbiter favours the older one: with equal work the younger one
-  // ended ~40 us later.  With sp.flip each wave flips its priority every
-  // step, in opposite phase to its partner, so the two advance at about the
-  // same rate.  (Beside prefill tiles, one decode wave per SIMD, it is off.)
-  const bool younger = uniform(w >= W / 2 ? 1 : 0) != 0;
-  const bool flip = sp.flip != 0;
-  for (;;) {
-    if (flip) {
-      if (younger) __builtin_amdgcn_s_setprio(1); else __builtin_amdgcn_s_setprio(0);
+  // sp.rounds waves share each SIMD (waves w, w + W / rounds, ... in
+  // dispatch order), and the issue arbiter favours the oldest: with equal
+  // work, the second of two waves ended ~40 us after the first.  Each wave
+  // steps its priority through 0 .. rounds - 1, one step per step of the
+  // walk, starting at its dispatch round, so the waves of a SIMD take turns
+  // at the top and advance at about the same rate.  (Beside prefill tiles,
+  // one decode wave per SIMD, rounds is 0: off.)
+  const int rounds = sp.rounds;
+  int ph = uniform(rounds > 1 ? (int)((long long)w * rounds / W) : 0);
+  auto next_priority = [&]() {
+    if (rounds > 1) {
+      if (ph == 0) __builtin_amdgcn_s_setprio(0);
+      else if (ph == 1) __builtin_amdgcn_s_setprio(1);
+      else if (ph == 2) __builtin_amdgcn_s_setprio(2);
+      else __builtin_amdgcn_s_setprio(3);
+      ph = ph + 1 == rounds ? 0 : ph + 1;
     }
+  };
+  for (;;) {
+    next_priority();
     StreamCur c2 = half_step(ra, rb, qa, qb, cur0, cur1, ids_b, ids_a, new0);
     if (!cur1.valid) break;
     cur0 = cur1;
     cur1 = c2;
     // ids_a now holds the ids of cur1's step (K/V -> ra)
-    if (flip) {
-      if (younger) __builtin_amdgcn_s_setprio(0); else __builtin_amdgcn_s_setprio(1);
-    }
+    next_priority();
     StreamCur c3 = half_step(rb, ra, qb, qa, cur0, cur1, ids_a, ids_b, new0);
     if (!cur1.valid) break;
     cur0 = cur1;
@@ -1612,7 +1619,7 @@ static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hi
   sp.waves = a.stream_waves;
   sp.c0 = a.stream_c0;
   sp.epoch = a.stream_epoch;
-  sp.flip = a.stream_flip ? 1 : 0;
+  sp.rounds = a.stream_rounds;
   sp.counters = a.stream_counters;
   sp.part_acc = a.stream_acc;
   sp.part_ml = a.stream_ml;
