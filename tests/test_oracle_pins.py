@@ -531,3 +531,96 @@ def test_prefix_cache_eviction_and_release_order():
     x = []
     pool2.append(x, 0, 32)                                 # takes 2 then 1: 1 is evicted
     assert pool2.key[1] is None and pool2.match_prefix(toks) == [0]
+
+
+# ------------------------------------------------------------ code decoding
+def test_decode_bf16_every_code_matches_torch():
+    """All 65,536 bf16 codes decode to the value torch's own bfloat16 type
+    gives them (NaN codes to NaN, the sign of zero kept): the stored bit
+    patterns are read as their exact values (Continuous batching +
+    PagedAttention 3.6 computes on the cached K/V as stored)."""
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = po.decode(codes, "bf16")
+    want = torch.from_numpy(codes.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    assert got.dtype == np.float64 and got.shape == codes.shape
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+
+
+def test_decode_format_values():
+    """Values the bf16 and binary32 formats fix, written out by hand."""
+    bf16 = {0x3F80: 1.0, 0xC000: -2.0, 0x3E80: 0.25, 0x4049: 3.140625,
+            0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126, 0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,
+            0x7F80: math.inf, 0xFF80: -math.inf}
+    for c, v in bf16.items():
+        assert po.decode(np.array([c], np.uint16), "bf16")[0] == v, hex(c)
+    assert math.copysign(1.0, po.decode(np.array([0x8000], np.uint16), "bf16")[0]) == -1.0
+    f32 = {0x3F800000: 1.0, 0xBF000000: -0.5, 0x00000001: 2.0 ** -149,
+           0x00800000: 2.0 ** -126, 0x7F7FFFFF: (2 - 2 ** -23) * 2.0 ** 127,
+           0x3DCCCCCD: 0.100000001490116119384765625}
+    for c, v in f32.items():
+        assert po.decode(np.array([c], np.uint32), "f32")[0] == v, hex(c)
+    assert math.isnan(po.decode(np.array([0x7FC00000], np.uint32), "f32")[0])
+
+
+def test_decode_f32_random_codes_match_torch():
+    """Random binary32 codes (normal, subnormal, NaN and infinite ones among
+    them), decoded in a strided 3-D view: same shape, and torch's float32
+    reading of every code."""
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 1 << 32, size=(8, 64, 66), dtype=np.uint64).astype(np.uint32)
+    codes[0, 0, :6] = [0x7F800000, 0xFF800000, 0x7FC00001, 0x00000001, 0x807FFFFF, 0x80000000]
+    view = codes[:, ::2, 1:65]
+    got = po.decode(view, "f32")
+    assert got.shape == view.shape and got.dtype == np.float64
+    want = torch.from_numpy(np.ascontiguousarray(view).view(np.int32)).view(torch.float32).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+    # bf16 decoding of a strided view keeps the shape and each element's value
+    b = workloads._bf16_codes(rng.standard_normal((4, 6, 10)).astype(np.float32))[:, 1::2, ::3]
+    gb = po.decode(b, "bf16")
+    assert gb.shape == b.shape
+    assert np.array_equal(gb, torch.from_numpy(np.ascontiguousarray(b).view(np.int16))
+                          .view(torch.bfloat16).double().numpy())
+
+
+# ------------------------------------------- logical-order reference rows
+def _check_sequence_attention_rows(w):
+    out = scenario.run_step(w)["out"]
+    qsl = w.query_start_loc
+    for s in range(w.batch):
+        got = scenario.sequence_attention(w, s)
+        assert got.shape == (int(w.q_len[s]), w.num_q_heads, w.head_size)
+        assert np.array_equal(got, out[qsl[s]:qsl[s + 1]]), f"{w.name}: sequence {s}"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_sequence_attention_equals_paged_step(cfg):
+    """The reference rows that full-size parity uses, computed from each
+    sequence's K/V in logical order straight from the draws, equal the
+    paged oracle step (allocator, copies, scatter, gather through the block
+    table) row for row and bit for bit."""
+    _check_sequence_attention_rows(workloads.small(cfg))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 5])
+def test_sequence_attention_equals_paged_step_fp8(cfg):
+    """The same on FP8 caches: quantized values, scales applied alike."""
+    _check_sequence_attention_rows(workloads.make_fp8(cfg, small_size=True))
+
+
+def test_sequence_attention_row_subsets_of_the_chunk():
+    """Row subsets of the prefill chunk (first rows, rows at block edges, the
+    last row, unsorted and repeated picks) equal those rows of the full step."""
+    w = workloads.small(4)
+    out = scenario.run_step(w)["out"]
+    s = int(np.argmax(w.q_len))
+    ql = int(w.q_len[s])
+    r0 = int(w.query_start_loc[s])
+    for rows in ([0], [ql - 1], [0, 1, 15, 16, 17, ql // 2, ql - 1], [ql - 1, 3, 3, 0]):
+        got = scenario.sequence_attention(w, s, rows)
+        assert np.array_equal(got, out[r0 + np.asarray(rows)]), rows
