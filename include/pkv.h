@@ -19,12 +19,17 @@
  *    ends.
  *  - GPU work is enqueued on `stream` (a hipStream_t; NULL = the null
  *    stream), asynchronously to the host.  No entry point synchronises or
- *    reads device memory from the host.
+ *    reads device memory from the host (except in the debug mode below).
  *  - Return value: PKV_OK (0) or a PKV_ERR_* code.  Arguments are checked on
  *    the host before anything is launched; on an error nothing is launched
  *    and pkv_last_error() describes it.  Contents of device buffers (slots,
  *    table entries, lengths) cannot be checked without a copy; they are the
- *    caller's preconditions, stated per call.
+ *    caller's preconditions, stated per call.  With the environment variable
+ *    PKV_DEBUG_VALIDATE=1 at the time of a call, the call copies that device
+ *    data to the host (after the stream's earlier work: it synchronises the
+ *    stream, so it cannot be captured into a graph) and checks it with the
+ *    pkv_validate_* functions below; a violation returns PKV_ERR_RANGE and
+ *    nothing is launched.
  *
  * KV pool layout (bytes; es = element size, E = 16 / es elements per
  * 16-byte granule, bs = block_size = 16, D = head_size):
@@ -59,6 +64,13 @@ enum {
   PKV_ERR_NOMEM = 6,     /* pkv_pool has too few free blocks                */
   PKV_ERR_RANGE = 7      /* a host-visible index or length is out of range  */
 };
+
+/* The pool layout described at the top of this file: pool[block][kv head]
+ * [K, V][tile], K tiles granule-major by d, V tiles granule-major by token,
+ * 16-byte granules.  pkv_layout() returns it, so a caller that views the pool
+ * as a tensor can check that it reads the layout this library writes. */
+enum { PKV_LAYOUT_HEAD_KV_GRANULE16 = 1 };
+int pkv_layout(void);
 
 /* Element types of a cache.  PKV_FP8_E4M3 stores OCP FP8 E4M3 codes (1 sign
  * bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7F and
@@ -185,7 +197,19 @@ size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads
  *   workspace     device, >= pkv_attention_workspace_bytes(...) bytes
  * A sequence of length 0 yields a zero row.  Preconditions on device data:
  * the first ceil(seq_lens[s]/16) table entries of row s are valid block
- * ids; the K/V of every position < seq_lens[s] were written. */
+ * ids; the K/V of every position < seq_lens[s] were written.
+ * Output is float32 only: the attention outputs are the fp32 accumulations
+ * themselves (a bf16 output would round them to 8 significant bits).
+ * Graph capture: a captured call replays correctly when the device
+ * seq_lens (and block tables) have changed since the capture, as in a
+ * decode loop where every length grows by one per step, provided every
+ * length stays <= max_blocks_per_seq * 16 and the workspace, which depends
+ * only on num_seqs, the head counts and the host lengths' wave count, is
+ * the captured one.  The host lengths only size the launch; the kernel
+ * plans its work from the device lengths.  (With PKV_DECODE_SPLIT=units the
+ * fixed-partition path is used instead, whose plan comes from the host
+ * lengths: a captured call of that path is valid only for the lengths it
+ * was captured with.) */
 int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
                            int32_t num_q_heads, const int32_t* block_tables,
                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
@@ -208,7 +232,10 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
  * joins it back (`stream` waits for an event recorded on the side stream),
  * so the work is still ordered by `stream` and can be captured from it.  The
  * side stream and its events are created by the first such call on a device;
- * make that call outside graph capture.
+ * make that call outside graph capture.  A captured mixed call is valid
+ * for the query_start_loc and the prefill rows' lengths it was captured
+ * with (they size the prefill grid and the workspace); its decode rows'
+ * lengths may change as for paged_attention_decode.
  * Host-checked: q_len_s <= seq_lens[s] <= max_blocks_per_seq * 16. */
 int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
                           int32_t num_q_heads, const int32_t* query_start_loc,
@@ -216,6 +243,37 @@ int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
                           const int32_t* h_seq_lens, const int32_t* block_tables,
                           int32_t max_blocks_per_seq, int32_t num_seqs, int64_t num_tokens,
                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* --------------------------------- preconditions on device data (debug) */
+/* Checks of the preconditions the calls above state on device data, run on
+ * host copies of that data (PKV_DEBUG_VALIDATE=1 runs them inside the calls;
+ * a caller may also run them itself).  PKV_OK, or PKV_ERR_RANGE with the
+ * first violation in pkv_last_error(); PKV_ERR_NULL / PKV_ERR_DIM for bad
+ * arguments. */
+
+/* paged_kv_write: every slot >= 0 is below num_blocks * 16, and no two
+ * tokens share a slot (negative slots are skipped).  slots: host int64
+ * [num_tokens]. */
+int pkv_validate_slots(const pkv_cache* cache, const int64_t* slots, int64_t num_tokens);
+
+/* block_copy (same_pool = 1) and block_swap (same_pool = 0): sources in
+ * [0, num_src_blocks), destinations in [0, num_dst_blocks) and distinct;
+ * with same_pool, no block is both a destination and a source.
+ * pairs: host int64 [num_pairs][2] = (src, dst). */
+int pkv_validate_block_pairs(const int64_t* pairs, int64_t num_pairs, int64_t num_src_blocks,
+                             int64_t num_dst_blocks, int32_t same_pool);
+
+/* paged_attention_decode (query_start_loc NULL) and paged_attention_mixed:
+ * seq_lens (and query_start_loc) equal their host copies when those are
+ * given (NULL skips the comparison); 0 <= seq_lens[s] <= max_blocks_per_seq
+ * * 16; q_len_s <= seq_lens[s]; and the first ceil(seq_lens[s] / 16) entries
+ * of table row s lie in [0, num_blocks).  Every pointer is host memory:
+ * block_tables int32 [num_seqs][max_blocks_per_seq], seq_lens int32
+ * [num_seqs], query_start_loc int32 [num_seqs + 1]. */
+int pkv_validate_attention(const pkv_cache* cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* h_seq_lens, const int32_t* query_start_loc,
+                           const int32_t* h_query_start_loc, int32_t num_seqs);
 
 /* ------------------------------------------------- host block allocator */
 /* A pool of block ids with reference counts (vLLM 技术内幕 section 2.1-2.2;

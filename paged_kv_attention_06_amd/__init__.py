@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     PKV_BF16,
     PKV_F32,
     PKV_FP8_E4M3,
+    PKV_LAYOUT_HEAD_KV_GRANULE16,
     Cache,
     PkvCache,
     PkvError,
@@ -23,6 +24,10 @@ from ._lib import (  # noqa: F401
     pkv_block_bytes,
     pkv_block_hash,
     pkv_build_slot_mapping,
+    pkv_layout,
+    pkv_validate_attention,
+    pkv_validate_block_pairs,
+    pkv_validate_slots,
     status_string,
     version,
 )

@@ -84,7 +84,18 @@ _c["pkv_pool_match_prefix"] = _sig("pkv_pool_match_prefix", ctypes.c_int,
 _c["pkv_pool_cache_blocks"] = _sig("pkv_pool_cache_blocks", ctypes.c_int,
                                    [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32])
 
+_c["pkv_layout"] = _sig("pkv_layout", ctypes.c_int, [])
+_c["pkv_validate_slots"] = _sig("pkv_validate_slots", ctypes.c_int,
+                                [ctypes.POINTER(PkvCache), _i64p, ctypes.c_int64])
+_c["pkv_validate_block_pairs"] = _sig("pkv_validate_block_pairs", ctypes.c_int,
+                                      [_i64p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int32])
+_c["pkv_validate_attention"] = _sig("pkv_validate_attention", ctypes.c_int,
+                                    [ctypes.POINTER(PkvCache), _i32p, ctypes.c_int32, _i32p,
+                                     _i32p, _i32p, _i32p, ctypes.c_int32])
+
 EXPORTED = tuple(_c)
+PKV_LAYOUT_HEAD_KV_GRANULE16 = 1
 
 
 class PkvError(RuntimeError):
@@ -133,6 +144,42 @@ def _stream(stream):
 
 def version() -> int:
     return _c["pkv_version"]()
+
+
+def pkv_layout() -> int:
+    return _c["pkv_layout"]()
+
+
+def _opt_i32(a):
+    return None if a is None else _ptr_i32(a)
+
+
+def pkv_validate_slots(desc: PkvCache, slots) -> None:
+    """Raises PkvError unless the host slots meet paged_kv_write's preconditions."""
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    _check(_c["pkv_validate_slots"](ctypes.byref(desc), _ptr_i64(s), s.shape[0]),
+           "pkv_validate_slots")
+
+
+def pkv_validate_block_pairs(pairs, num_src_blocks: int, num_dst_blocks: int,
+                             same_pool: bool) -> None:
+    p = np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    _check(_c["pkv_validate_block_pairs"](_ptr_i64(p), p.shape[0], num_src_blocks,
+                                          num_dst_blocks, int(same_pool)),
+           "pkv_validate_block_pairs")
+
+
+def pkv_validate_attention(desc: PkvCache, block_tables, seq_lens, h_seq_lens=None,
+                           query_start_loc=None, h_query_start_loc=None) -> None:
+    bt = _host_i32(block_tables)
+    sl = _host_i32(seq_lens)
+    hsl = None if h_seq_lens is None else _host_i32(h_seq_lens)
+    qsl = None if query_start_loc is None else _host_i32(query_start_loc)
+    hqsl = None if h_query_start_loc is None else _host_i32(h_query_start_loc)
+    _check(_c["pkv_validate_attention"](ctypes.byref(desc), _ptr_i32(bt),
+                                        bt.shape[1] if bt.ndim == 2 else 0, _ptr_i32(sl),
+                                        _opt_i32(hsl), _opt_i32(qsl), _opt_i32(hqsl),
+                                        sl.shape[0]), "pkv_validate_attention")
 
 
 def status_string(status: int) -> str:

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <deque>
+#include <algorithm>
 #include <new>
 #include <string>
 #include <unordered_map>
@@ -81,6 +82,45 @@ int check_cache(const pkv_cache* c, pkv::CacheDesc* d, bool need_kv = true) {
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// PKV_DEBUG_VALIDATE=1: every entry point copies the device data it is
+// about to use (slots, pairs, tables, lengths) to the host after the
+// stream's earlier work and checks the preconditions that pkv.h states on
+// it (pkv_validate_*), so a bad entry is reported instead of launched.
+bool debug_validate() {
+  const char* e = std::getenv("PKV_DEBUG_VALIDATE");
+  return e && e[0] == '1' && e[1] == '\0';
+}
+
+template <typename T>
+int fetch(std::vector<T>& dst, const T* src, size_t n, void* stream, const char* what) {
+  dst.resize(n > 0 ? n : 1);  // data() of an empty copy is still a valid pointer
+  if (n == 0) return PKV_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess)
+    return fail(PKV_ERR_HIP, "PKV_DEBUG_VALIDATE: copy of %s to the host: %s", what,
+                hipGetErrorString(e));
+  return PKV_OK;
+}
+
+// First repeated value of v (indices into the original order), or false.
+bool first_repeat(const std::vector<int64_t>& v, int64_t* a, int64_t* b) {
+  std::vector<int64_t> idx(v.size());
+  for (size_t i = 0; i < v.size(); ++i) idx[i] = (int64_t)i;
+  std::sort(idx.begin(), idx.end(), [&v](int64_t x, int64_t y) {
+    return v[(size_t)x] != v[(size_t)y] ? v[(size_t)x] < v[(size_t)y] : x < y;
+  });
+  for (size_t i = 1; i < idx.size(); ++i) {
+    if (v[(size_t)idx[i]] == v[(size_t)idx[i - 1]]) {
+      *a = idx[i - 1];
+      *b = idx[i];
+      return true;
+    }
+  }
+  return false;
 }
 
 struct Plan {
@@ -268,6 +308,19 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   const size_t need = wl.total;
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+  if (debug_validate()) {
+    std::vector<int32_t> bt, sl, qv;
+    if (int e = fetch(bt, block_tables, (size_t)num_seqs * (size_t)max_blocks, stream,
+                      "block_tables"))
+      return e;
+    if (int e = fetch(sl, seq_lens, (size_t)num_seqs, stream, "seq_lens")) return e;
+    if (mixed)
+      if (int e = fetch(qv, qsl, (size_t)num_seqs + 1, stream, "query_start_loc")) return e;
+    if (int e = pkv_validate_attention(cache, bt.data(), max_blocks, sl.data(), h_seq_lens,
+                                       mixed ? qv.data() : nullptr, mixed ? h_qsl : nullptr,
+                                       num_seqs))
+      return e;
+  }
   pkv::AttnDesc a;
   a.out = out;
   a.q = q;
@@ -298,7 +351,11 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.stream_waves = 0;
   a.stream_rounds = 0;
   const bool mixed_call = plan.prefill_tiles > 0 && plan.decode_units > 0;
-  if (plan.decode_units > 0 && (stream_decode_enabled() || c.fp8) &&
+  // A decode call whose rows are all empty still runs one stream wave, which
+  // writes their zero rows (and, replayed from a graph after the lengths
+  // grew, walks them).
+  const bool decode_rows = plan.decode_units > 0 || (!mixed && num_seqs > 0);
+  if (decode_rows && (stream_decode_enabled() || c.fp8) &&
       (!mixed_call || mixed_concurrent_enabled())) {
     const int G = num_q_heads / c.hkv;
     // Beside prefill tiles the decode keeps one wave per SIMD: a SIMD then
@@ -306,6 +363,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
     const int slots = mixed_call ? 4 * pkv::device_cus()
                                  : pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
     int64_t waves = stream_wave_cap(plan, c.hkv);
+    if (waves < 1) waves = 1;
     if (slots > 0 && slots < waves) waves = slots;
     if (const char* e = std::getenv("PKV_STREAM_WAVES")) {  // tuning: cap the waves
       const long long cap = std::atoll(e);
@@ -313,7 +371,6 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
     }
     if (slots > 0) {
       static std::atomic<unsigned> epoch{first_epoch()};
-      a.stream_total = stream_total(plan, c.hkv);
       a.stream_waves = (int)waves;
       a.stream_c0 = pkv::kStreamSetupCost;
       a.stream_epoch = epoch.fetch_add(2, std::memory_order_relaxed);
@@ -322,12 +379,15 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
       const int simds = 4 * pkv::device_cus();
       const int64_t rounds = simds > 0 ? (waves + simds - 1) / simds : 0;
       a.stream_rounds = (!mixed_call && rounds > 1) ? (int)(rounds < 4 ? rounds : 4) : 0;
-      a.stream_acc = reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader);
-      a.stream_ml = reinterpret_cast<float*>(ws + wl.st_ml_off);
-      a.stream_counters = reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off);
+      // (no decode region when every row is empty: one wave, nothing split)
+      const bool region = ws && plan.decode_units > 0;
+      a.stream_acc = region ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;
+      a.stream_ml = region ? reinterpret_cast<float*>(ws + wl.st_ml_off) : nullptr;
+      a.stream_counters =
+          region ? reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off) : nullptr;
     }
   }
-  if (c.fp8 && plan.decode_units > 0 && a.stream_waves == 0)
+  if (c.fp8 && decode_rows && a.stream_waves == 0)
     return fail(PKV_ERR_HIP, "fp8 decode needs the device's wave count (hipGetDevice failed)");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.prefill_tiles > 0 && plan.decode_units > 0)
@@ -402,6 +462,11 @@ int paged_kv_write(const pkv_cache* cache, const void* k_new, const void* v_new,
   if (num_tokens < 0) return fail(PKV_ERR_DIM, "num_tokens %lld < 0", (long long)num_tokens);
   if (num_tokens == 0) return ok();
   if (!k_new || !v_new || !slot_mapping) return fail(PKV_ERR_NULL, "k_new, v_new or slot_mapping is NULL");
+  if (debug_validate()) {
+    std::vector<int64_t> sv;
+    if (int e = fetch(sv, slot_mapping, (size_t)num_tokens, stream, "slot_mapping")) return e;
+    if (int e = pkv_validate_slots(cache, sv.data(), num_tokens)) return e;
+  }
   return hip_status(pkv::launch_kv_write(c, k_new, v_new, slot_mapping, num_tokens,
                                          static_cast<hipStream_t>(stream)),
                     "paged_kv_write");
@@ -413,6 +478,12 @@ int block_copy(const pkv_cache* cache, const int64_t* pairs, int64_t num_pairs, 
   if (num_pairs < 0) return fail(PKV_ERR_DIM, "num_pairs %lld < 0", (long long)num_pairs);
   if (num_pairs == 0) return ok();
   if (!pairs) return fail(PKV_ERR_NULL, "pairs is NULL");
+  if (debug_validate()) {
+    std::vector<int64_t> pv;
+    if (int e = fetch(pv, pairs, 2 * (size_t)num_pairs, stream, "pairs")) return e;
+    if (int e = pkv_validate_block_pairs(pv.data(), num_pairs, c.num_blocks, c.num_blocks, 1))
+      return e;
+  }
   return hip_status(pkv::launch_block_copy(c, pairs, num_pairs, static_cast<hipStream_t>(stream)),
                     "block_copy");
 }
@@ -429,6 +500,14 @@ int block_swap(const pkv_cache* cache, void* host_kv, int64_t num_host_blocks,
   if (num_pairs == 0) return ok();
   if (!host_kv || !pairs) return fail(PKV_ERR_NULL, "host_kv or pairs is NULL");
   if (num_host_blocks < 1) return fail(PKV_ERR_DIM, "the host pool has no blocks");
+  if (debug_validate()) {
+    std::vector<int64_t> pv;
+    if (int e = fetch(pv, pairs, 2 * (size_t)num_pairs, stream, "pairs")) return e;
+    const bool out = direction == PKV_SWAP_OUT;
+    if (int e = pkv_validate_block_pairs(pv.data(), num_pairs, out ? c.num_blocks : num_host_blocks,
+                                         out ? num_host_blocks : c.num_blocks, 0))
+      return e;
+  }
   void* dev = nullptr;
   if (hipHostGetDevicePointer(&dev, host_kv, 0) != hipSuccess || !dev) {
     (void)hipGetLastError();
@@ -471,6 +550,113 @@ int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q, int
   return attention(cache, out, q, num_q_heads, query_start_loc, seq_lens, h_query_start_loc,
                    h_seq_lens, block_tables, max_blocks_per_seq, num_seqs, num_tokens, scale,
                    workspace, workspace_bytes, stream, true);
+}
+
+// ---------------------------------------------------------------------------
+// preconditions on device data, checked on host copies
+// ---------------------------------------------------------------------------
+int pkv_layout(void) { return PKV_LAYOUT_HEAD_KV_GRANULE16; }
+
+int pkv_validate_slots(const pkv_cache* cache, const int64_t* slots, int64_t num_tokens) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c, false)) return e;
+  if (num_tokens < 0) return fail(PKV_ERR_DIM, "num_tokens %lld < 0", (long long)num_tokens);
+  if (num_tokens > 0 && !slots) return fail(PKV_ERR_NULL, "slots is NULL");
+  const int64_t cap = c.num_blocks * pkv::kBlockSize;
+  std::vector<int64_t> used, tok;
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int64_t sl = slots[t];
+    if (sl < 0) continue;
+    if (sl >= cap)
+      return fail(PKV_ERR_RANGE, "slot_mapping[%lld] = %lld is not below num_blocks * 16 = %lld",
+                  (long long)t, (long long)sl, (long long)cap);
+    used.push_back(sl);
+    tok.push_back(t);
+  }
+  int64_t a = 0, b = 0;
+  if (first_repeat(used, &a, &b))
+    return fail(PKV_ERR_RANGE, "slot %lld is written by tokens %lld and %lld",
+                (long long)used[(size_t)a], (long long)tok[(size_t)a], (long long)tok[(size_t)b]);
+  return ok();
+}
+
+int pkv_validate_block_pairs(const int64_t* pairs, int64_t num_pairs, int64_t num_src_blocks,
+                             int64_t num_dst_blocks, int32_t same_pool) {
+  if (num_pairs < 0 || num_src_blocks < 0 || num_dst_blocks < 0)
+    return fail(PKV_ERR_DIM, "negative count");
+  if (num_pairs > 0 && !pairs) return fail(PKV_ERR_NULL, "pairs is NULL");
+  std::vector<int64_t> dst((size_t)num_pairs);
+  for (int64_t i = 0; i < num_pairs; ++i) {
+    const int64_t a = pairs[2 * i], b = pairs[2 * i + 1];
+    if (a < 0 || a >= num_src_blocks)
+      return fail(PKV_ERR_RANGE, "pair %lld: source block %lld outside [0, %lld)", (long long)i,
+                  (long long)a, (long long)num_src_blocks);
+    if (b < 0 || b >= num_dst_blocks)
+      return fail(PKV_ERR_RANGE, "pair %lld: destination block %lld outside [0, %lld)",
+                  (long long)i, (long long)b, (long long)num_dst_blocks);
+    dst[(size_t)i] = b;
+  }
+  int64_t x = 0, y = 0;
+  if (first_repeat(dst, &x, &y))
+    return fail(PKV_ERR_RANGE, "block %lld is the destination of pairs %lld and %lld",
+                (long long)dst[(size_t)x], (long long)x, (long long)y);
+  if (same_pool) {
+    std::vector<int64_t> sorted = dst;
+    std::sort(sorted.begin(), sorted.end());
+    for (int64_t i = 0; i < num_pairs; ++i) {
+      const int64_t a = pairs[2 * i];
+      if (std::binary_search(sorted.begin(), sorted.end(), a)) {
+        int64_t j = 0;
+        while (dst[(size_t)j] != a) ++j;
+        return fail(PKV_ERR_RANGE, "block %lld is the destination of pair %lld and the source of "
+                    "pair %lld", (long long)a, (long long)j, (long long)i);
+      }
+    }
+  }
+  return ok();
+}
+
+int pkv_validate_attention(const pkv_cache* cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                           const int32_t* h_seq_lens, const int32_t* query_start_loc,
+                           const int32_t* h_query_start_loc, int32_t num_seqs) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c, false)) return e;
+  if (num_seqs < 0 || max_blocks_per_seq < 0) return fail(PKV_ERR_DIM, "negative count");
+  if (num_seqs == 0) return ok();
+  if (!block_tables || !seq_lens) return fail(PKV_ERR_NULL, "block_tables or seq_lens is NULL");
+  const int32_t* qsl = query_start_loc;
+  if (qsl) {
+    for (int32_t s = 0; s <= num_seqs; ++s) {
+      if (h_query_start_loc && qsl[s] != h_query_start_loc[s])
+        return fail(PKV_ERR_RANGE, "query_start_loc[%d] = %d, but %d in the host copy", s,
+                    qsl[s], h_query_start_loc[s]);
+    }
+    if (qsl[0] != 0) return fail(PKV_ERR_RANGE, "query_start_loc[0] = %d, must be 0", qsl[0]);
+  }
+  const int64_t cap = (int64_t)max_blocks_per_seq * pkv::kBlockSize;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t L = seq_lens[s];
+    if (h_seq_lens && L != h_seq_lens[s])
+      return fail(PKV_ERR_RANGE, "seq_lens[%d] = %lld, but %d in the host copy", s, (long long)L,
+                  h_seq_lens[s]);
+    if (L < 0 || L > cap)
+      return fail(PKV_ERR_RANGE, "seq_lens[%d] = %lld outside [0, max_blocks_per_seq * 16 = %lld]",
+                  s, (long long)L, (long long)cap);
+    if (qsl) {
+      const int64_t ql = (int64_t)qsl[s + 1] - qsl[s];
+      if (ql < 0 || ql > L)
+        return fail(PKV_ERR_RANGE, "sequence %d has %lld query rows and length %lld", s,
+                    (long long)ql, (long long)L);
+    }
+    const int32_t* row = block_tables + (size_t)s * max_blocks_per_seq;
+    for (int64_t j = 0; j < (L + pkv::kBlockSize - 1) / pkv::kBlockSize; ++j) {
+      if (row[j] < 0 || row[j] >= c.num_blocks)
+        return fail(PKV_ERR_RANGE, "block_tables[%d][%lld] = %d outside [0, %lld)", s,
+                    (long long)j, row[j], (long long)c.num_blocks);
+    }
+  }
+  return ok();
 }
 
 // ---------------------------------------------------------------------------

@@ -67,7 +67,6 @@ struct AttnDesc {
   char* ws_v;                      // fp16 V tiles of those blocks [vblock][hkv][16 * D]
   int32_t* ws_vexp;                // their power-of-two scale exponents [hkv][vblock]
   // stream decode (stream_waves > 0 selects it)
-  int64_t stream_total;            // cost of all (row, kv head) items
   int stream_waves;                // ranges / waves of the launch
   int stream_c0;                   // setup charge per item
   unsigned stream_epoch;           // distinct per call

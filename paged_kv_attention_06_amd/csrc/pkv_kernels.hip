@@ -732,8 +732,17 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int item, cha
   finish(cur);
 }
 
+// Waves per SIMD the decode kernels are compiled for: two, except where
+// their registers do not fit in half the register file (fp32 at D = 128 or
+// G = 8; bf16 at D = 128 and G = 8): those get one wave per SIMD and all 512
+// registers, so nothing spills to memory.
+constexpr int decode_waves_per_simd(int es, int d, int g) {
+  return (es == 4 && (d == 128 || g == 8)) || (es == 2 && d == 128 && g == 8) ? 1 : 2;
+}
+
 template <int ES, int D, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_partition(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    decode_waves_per_simd(ES, D, G)))) void k_decode_partition(
     DecodeParams p) {
   __shared__ __align__(16) char lds[DecodeLds<ES, D, G>::BYTES];
   decode_item<ES, D, G>(p, blockIdx.x, lds);
@@ -872,7 +881,6 @@ __device__ __forceinline__ void wait_stores() {
 
 struct StreamParams {
   DecodeParams d;
-  long long total;               // cost of all items
   int waves;                     // ranges = grid size
   int c0;                        // setup charge per item, in steps
   unsigned epoch;                // distinct per call
@@ -1003,8 +1011,8 @@ __device__ __forceinline__ void stream_merge(const StreamParams& sp, int wA, int
 }
 
 template <int ES, int D, int G>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_decode_stream(
-    StreamParams sp) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
+    decode_waves_per_simd(ES, D, G)))) void k_decode_stream(StreamParams sp) {
   using S = DecodeShape<ES, D>;
   constexpr int QBUF = StreamLds<ES, D, G>::QBUF;
   constexpr int QGR = G * S::QKG;            // 16-byte granules of one item's q rows
@@ -1018,7 +1026,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x;
   const int W = sp.waves;
-  const long long T = sp.total;
   const int hkv = p.hkv;
   const int hq = hkv * G;
   const int c0 = sp.c0;
@@ -1045,6 +1052,49 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
     }
   };
 
+  // ---- the cost line, from the device lengths.  Lane l holds sequences
+  // 4l .. 4l + 3 of every chunk of 256.  The host's copy of the lengths only
+  // sized the grid: a call replayed from a captured graph after the lengths
+  // have changed still covers every item (the grid and the workspace depend
+  // on the wave count and the number of sequences, not on the lengths).
+  auto cost_of = [&](int L) -> long long {
+    return L > 0 ? (long long)hkv * ((L + 31) / 32 + c0) : 0;
+  };
+  struct ChunkCost {
+    long long c[4], tot, incl;  // this lane's costs, their sum, inclusive scan over lanes
+  };
+  auto chunk_cost = [&](int first) {
+    ChunkCost r;
+    r.tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int s = first + 4 * lane + k;
+      r.c[k] = cost_of(s < p.num_seqs ? row_len(p.seq_lens, p.qsl, s) : 0);
+      r.tot += r.c[k];
+    }
+    r.incl = r.tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long t = __shfl_up(r.incl, off);
+      if (lane >= off) r.incl += t;
+    }
+    return r;
+  };
+  const ChunkCost first = chunk_cost(0);
+  const long long first_total = uniform64(__shfl(first.incl, 63));
+  long long T = first_total;
+  if (p.num_seqs > 256) {
+    long long rest = 0;
+    for (int sb = 256; sb < p.num_seqs; sb += 256) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int s = sb + 4 * lane + k;
+        if (s < p.num_seqs) rest += cost_of(row_len(p.seq_lens, p.qsl, s));
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) rest += __shfl_xor(rest, off);
+    T += uniform64(rest);
+  }
   const long long cs = (long long)w * T / W;
   const long long ce = (long long)(w + 1) * T / W;
   if (cs >= ce) {
@@ -1056,12 +1106,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   // decode lengths (and output rows) in LDS for the walk
   int s0 = 0;
   long long base = 0;  // cost before sequence s0
-  auto cost_of = [&](int L) -> long long {
-    return L > 0 ? (long long)hkv * ((L + 31) / 32 + c0) : 0;
-  };
-  auto load_chunk = [&](int first) {
+  auto load_chunk = [&](int first_seq) {
     for (int k = 0; k < 4; ++k) {
-      const int s = first + 4 * lane + k;
+      const int s = first_seq + 4 * lane + k;
       len_lds[4 * lane + k] = s < p.num_seqs ? row_len(p.seq_lens, p.qsl, s) : 0;
       row_lds[4 * lane + k] = s < p.num_seqs ? (p.qsl ? p.qsl[s] : s) : 0;
     }
@@ -1069,44 +1116,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void k_
   };
   int s_found = -1;
   long long S_found = 0;
-  for (s0 = 0; s0 < p.num_seqs; s0 += 256) {
-    int len[4];
-    long long c[4], tot = 0;
+  auto pick = [&](const ChunkCost& cc) {  // cs lies in the chunk starting at s0
+    const unsigned long long m = __ballot(base + cc.incl > cs);
+    const int hit = __ffsll(m) - 1;
+    long long start = base + cc.incl - cc.tot;  // cost before this lane's first sequence
+    int kk = 3;
+    long long Sk = start;
+    bool found = false;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int s = s0 + 4 * lane + k;
-      len[k] = s < p.num_seqs ? row_len(p.seq_lens, p.qsl, s) : 0;
-      c[k] = cost_of(len[k]);
-      tot += c[k];
-    }
-    long long incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
-    const long long total = uniform64(__shfl(incl, 63));
-    if (cs < base + total) {
-      const unsigned long long m = __ballot(base + incl > cs);
-      const int hit = __ffsll(m) - 1;
-      long long start = base + incl - tot;  // cost before this lane's first sequence
-      int kk = 3;
-      long long Sk = start;
-      bool found = false;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (!found && cs < start + c[k]) {
-          kk = k;
-          Sk = start;
-          found = true;
-        }
-        start += c[k];
+      if (!found && cs < start + cc.c[k]) {
+        kk = k;
+        Sk = start;
+        found = true;
       }
-      s_found = uniform(__shfl(s0 + 4 * lane + kk, hit));
-      S_found = uniform64(__shfl(Sk, hit));
-      break;
+      start += cc.c[k];
     }
-    base += total;
+    s_found = uniform(__shfl(s0 + 4 * lane + kk, hit));
+    S_found = uniform64(__shfl(Sk, hit));
+  };
+  if (cs < first_total) {
+    pick(first);
+  } else {
+    base = first_total;
+    for (s0 = 256; s0 < p.num_seqs; s0 += 256) {
+      const ChunkCost cc = chunk_cost(s0);
+      const long long total = uniform64(__shfl(cc.incl, 63));
+      if (cs < base + total) {
+        pick(cc);
+        break;
+      }
+      base += total;
+    }
   }
   if (s_found < 0) {
     zero_rows();
@@ -1615,7 +1656,6 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
 static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hipStream_t stream) {
   StreamParams sp;
   sp.d = make_decode_params(c, a);
-  sp.total = a.stream_total;
   sp.waves = a.stream_waves;
   sp.c0 = a.stream_c0;
   sp.epoch = a.stream_epoch;

@@ -56,20 +56,22 @@ def test_small_workload_full_parity(cfg):
     _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, f"small {w.name}")
 
 
-def _sample_seqs(w, k=6, seed=0):
-    rng = np.random.default_rng(seed)
-    L = w.seq_lens
-    picks = {int(np.argmax(L)), int(np.argmin(L)), 0, w.batch - 1}
-    picks.update(int(i) for i in rng.choice(w.batch, size=min(k, w.batch), replace=False))
-    if np.any(w.fork_of >= 0):
-        picks.add(int(np.flatnonzero(w.fork_of >= 0)[0]))
-    return sorted(picks)
+def _blocks_of(st, w, ids):
+    """Codes of whole blocks [n][Hkv][2][16 D] gathered on the GPU."""
+    bb = st.block_bytes
+    es = st.es
+    view = st.kv.view(w.num_blocks, bb)
+    idx = torch.as_tensor(np.asarray(ids, np.int64), device=st.kv.device)
+    raw = view.index_select(0, idx).cpu().numpy().view({1: np.uint8, 2: np.uint16, 4: np.uint32}[es])
+    return raw.reshape(len(ids), w.num_kv_heads, 2, 16 * w.head_size)
 
 
 @pytest.mark.parametrize("cfg", [2, 3, 5, 4])
-def test_full_size_sampled_parity(cfg):
-    """Full-size workload in the bench's launch configuration; sampled rows
-    against the oracle, plus the step's written slots and COW copies."""
+def test_full_size_parity(cfg):
+    """Full-size workload in the bench's launch configuration: every decode
+    row against the oracle (for the mixed step also every 5th row of the
+    chunk and its last), every written token at the oracle's slot with its
+    drawn values, and every copy-on-write destination equal to its source."""
     w = workloads.make(cfg)
     _announce(f"full {w.name}: B={w.batch} T={w.num_tokens} blocks={w.num_blocks}")
     st = gpu_step.run_workload(w)
@@ -77,12 +79,11 @@ def test_full_size_sampled_parity(cfg):
     assert np.all(np.isfinite(out)), "non-finite output"
     qsl = w.query_start_loc
     got, want = [], []
-    for s in _sample_seqs(w):
+    for s in range(w.batch):
         q_len = int(w.q_len[s])
-        rows = list(range(q_len)) if q_len <= 8 else [0, 1, q_len // 2, q_len - 2, q_len - 1]
-        ref = scenario.sequence_attention(w, s, rows)
+        rows = [0] if q_len == 1 else sorted(set(range(0, q_len, 5)) | {q_len - 1})
+        want.append(scenario.sequence_attention(w, s, rows))
         got.append(out[qsl[s] + np.asarray(rows)])
-        want.append(ref)
     _check_attention(np.concatenate(got), np.concatenate(want), w.dtype, f"full {w.name}")
 
     # the step's written tokens sit at the oracle's slots with their drawn values
@@ -91,25 +92,23 @@ def test_full_size_sampled_parity(cfg):
     assert np.array_equal(st.h_cow, tabs["cow_pairs"])
     kidx = po.k_tile_index(w.head_size, w.dtype)
     vidx = po.v_tile_index(w.head_size, w.dtype)
-    code = np.uint16 if w.dtype == "bf16" else np.uint32
-    bb = 2 * 16 * w.num_kv_heads * w.head_size * w.dtype_bytes
-    kv = st.kv.view(-1)
-    pick = np.unique(np.linspace(0, len(tabs["slots"]) - 1, 16).astype(int))
-    for t in pick:
-        slot = int(tabs["slots"][t])
-        blk, off = divmod(slot, 16)
-        raw = kv[blk * bb:(blk + 1) * bb].cpu().numpy().view(code)
-        raw = raw.reshape(w.num_kv_heads, 2, 16 * w.head_size)
-        assert np.array_equal(raw[:, 0, kidx[off]], w.new_k[t]), f"K of token {t}"
-        assert np.array_equal(raw[:, 1, vidx[off]], w.new_v[t]), f"V of token {t}"
-    # a COW destination holds the source's first (partial) tokens
-    for src, dst in tabs["cow_pairs"][:3]:
-        a = kv[src * bb:(src + 1) * bb].cpu().numpy().view(code).reshape(w.num_kv_heads, 2, -1)
-        b = kv[dst * bb:(dst + 1) * bb].cpu().numpy().view(code).reshape(w.num_kv_heads, 2, -1)
+    slots = tabs["slots"]
+    for a in range(0, len(slots), 512):
+        part = slots[a:a + 512]
+        blocks = _blocks_of(st, w, part // 16)
+        for i, slot in enumerate(part):
+            off = int(slot) % 16
+            t = a + i
+            assert np.array_equal(blocks[i, :, 0][:, kidx[off]], w.new_k[t]), f"K of token {t}"
+            assert np.array_equal(blocks[i, :, 1][:, vidx[off]], w.new_v[t]), f"V of token {t}"
+    # a copy-on-write destination holds its source's tokens before the append
+    pairs = tabs["cow_pairs"]
+    if len(pairs):
+        src, dst = _blocks_of(st, w, pairs[:, 0]), _blocks_of(st, w, pairs[:, 1])
         n_old = int(w.prompt_len[0]) % 16
         for off in range(n_old):
-            assert np.array_equal(a[:, 0, kidx[off]], b[:, 0, kidx[off]])
-            assert np.array_equal(a[:, 1, vidx[off]], b[:, 1, vidx[off]])
+            assert np.array_equal(src[:, :, 0][:, :, kidx[off]], dst[:, :, 0][:, :, kidx[off]])
+            assert np.array_equal(src[:, :, 1][:, :, vidx[off]], dst[:, :, 1][:, :, vidx[off]])
 
 
 def test_decode_is_deterministic_and_layout_invariant():
@@ -270,13 +269,12 @@ def test_fused_mixed_path(size, monkeypatch):
         _check_attention(fused, ref, "bf16", "fused mixed")
         _check_attention(concurrent, ref, "bf16", "concurrent mixed")
     else:
-        seqs = _sample_seqs(w)
-        for s in seqs:
-            rows = slice(int(w.query_start_loc[s]), int(w.query_start_loc[s + 1]))
-            if rows.stop - rows.start > 1:
-                continue  # the chunk's rows: checked against the oracle elsewhere
-            ref = scenario.sequence_attention(w, s)
-            _check_attention(fused[rows], ref, "bf16", f"fused row {s}")
+        qsl = w.query_start_loc
+        for s in range(w.batch):
+            q_len = int(w.q_len[s])
+            rows = [0] if q_len == 1 else sorted(set(range(0, q_len, 7)) | {q_len - 1})
+            ref = scenario.sequence_attention(w, s, rows)
+            _check_attention(fused[qsl[s] + np.asarray(rows)], ref, "bf16", f"fused sequence {s}")
     assert float(np.abs(fused - concurrent).max()) <= MAX_ABS_BF16, "fused and concurrent paths differ"
 
 
@@ -380,16 +378,15 @@ def test_fp8_small_workload_full_parity(cfg):
 
 
 @pytest.mark.parametrize("cfg", [3, 5])
-def test_fp8_full_size_sampled_parity(cfg):
+def test_fp8_full_size_parity(cfg):
+    """FP8 cache at full size: every decode row against the oracle."""
     w = workloads.make_fp8(cfg)
     _announce(f"fp8 full {w.name}: B={w.batch} blocks={w.num_blocks}")
     st = gpu_step.run_workload(w)
     out = st.out.cpu().numpy()
     assert np.all(np.isfinite(out))
-    rows = _sample_seqs(w)
-    want = np.concatenate([scenario.sequence_attention(w, s) for s in rows])
-    got = np.concatenate([out[s:s + 1] for s in rows])
-    _check_attention(got, want, "bf16", f"fp8 full {w.name}")
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in range(w.batch)])
+    _check_attention(out, want, "bf16", f"fp8 full {w.name}")
 
 
 def test_fp8_every_code_decodes_exactly():
@@ -433,17 +430,15 @@ def test_verify_small_full_parity():
     _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", "verify small")
 
 
-def test_verify_full_size_sampled_parity():
+def test_verify_full_size_parity():
+    """The full verify batch: every query row of every sequence."""
     w = workloads.make_verify()
     _announce(f"verify full: B={w.batch} T={w.num_tokens}")
     st = gpu_step.run_workload(w)
     out = st.out.cpu().numpy()
     assert np.all(np.isfinite(out))
-    qsl = w.query_start_loc
-    seqs = _sample_seqs(w)
-    got = np.concatenate([out[qsl[s]:qsl[s + 1]] for s in seqs])
-    want = np.concatenate([scenario.sequence_attention(w, s) for s in seqs])
-    _check_attention(got, want, "bf16", "verify full")
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in range(w.batch)])
+    _check_attention(out, want, "bf16", "verify full")
 
 
 # ------------------------------------------------------------------ block swap
@@ -604,3 +599,114 @@ def test_mixed_paths_group_and_head_sizes(G, D, mode, monkeypatch):
     st = gpu_step.run_workload(w)
     ref = scenario.run_step(w)
     _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"mixed {mode} G={G} D={D}")
+
+
+# --------------------------------- 8 query heads per kv head; fp32 at head size 128
+@pytest.mark.parametrize("kv,G,D", [("bf16", 8, 128), ("bf16", 8, 64), ("fp8", 8, 128),
+                                    ("fp8", 8, 64), ("f32", 1, 128), ("f32", 4, 128),
+                                    ("f32", 8, 128), ("f32", 8, 64)])
+def test_decode_wide_groups_and_fp32_head128(kv, G, D):
+    """Decode shapes the library accepts beyond the workloads' own: 8 query
+    heads per kv head (bf16 and FP8 caches) and fp32 caches at head size 128,
+    whose kernels run one wave per SIMD where their registers need it.
+    Lengths at block and step edges and one 5000-token row split over many
+    waves; the pool bit for bit and every row against the oracle."""
+    L = np.array([1, 16, 17, 33, 300, 1024, 5000, 64, 2], np.int32)
+    hkv = 2
+    dtype = "f32" if kv == "f32" else "bf16"
+    streams = [np.random.default_rng(x) for x in (101 + G, 102 + D, 103, 104 + len(kv))]
+    pool = int(1.25 * sum((int(x) + 15) // 16 for x in L)) + 8
+    w = workloads._build(3, f"decode {kv} G={G} D={D}", dtype, hkv * G, hkv, D, D ** -0.5, L - 1,
+                         np.ones(len(L), np.int32), pool, streams,
+                         cache_dtype="fp8" if kv == "fp8" else "",
+                         kv_scale=workloads.FP8_SCALE if kv == "fp8" else 1.0)
+    _announce(f"decode {kv} G={G} D={D}: L={L.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"]), "pool differs from the oracle's"
+    _check_attention(st.out.cpu().numpy(), ref["out"], dtype, f"decode {kv} G={G} D={D}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_batch_of_empty_rows_is_zero(kv):
+    """A decode call whose every sequence has length 0 returns PKV_OK and
+    writes zero rows (the oracle's reading of an empty sequence)."""
+    w = workloads.small(3) if kv == "bf16" else workloads.make_fp8(3, small_size=True)
+    _announce(f"all-empty decode batch, {kv}")
+    st = gpu_step.PagedStep(w)
+    st.build_history()
+    st.prepare_step()
+    st.h_seq_lens = np.zeros_like(st.h_seq_lens)
+    st.seq_lens = torch.from_numpy(st.h_seq_lens).cuda()
+    st.out.fill_(7.0)
+    st.attend()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(st.out).item() == 0
+
+
+def test_graph_replay_follows_growing_lengths():
+    """A decode call captured once and replayed for three more decode steps:
+    before each replay every sequence appends one token through the
+    library's allocator (new blocks enter the same table tensor), its K/V
+    are written, and the device lengths grow by one.  The replay plans its
+    work from the device lengths, so every row matches the oracle at the
+    new lengths."""
+    from paged_kv_attention_06_amd import _lib as L
+    w = workloads.make(3, batch=64)
+    _announce(f"graph replay with growing lengths: B={w.batch}")
+    st = gpu_step.PagedStep(w)
+    st.max_blocks += 1
+    st.tables = np.zeros((w.batch, st.max_blocks), np.int32)
+    st.build_history()
+    st.prepare_step()
+    st.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.attend()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    Ks = [scenario.sequence_kv(w, s)[0] for s in range(w.batch)]
+    Vs = [scenario.sequence_kv(w, s)[1] for s in range(w.batch)]
+    lens = w.seq_lens.astype(np.int32).copy()
+    for step in range(3):
+        shape = (w.batch, w.num_kv_heads, w.head_size)
+        k_new = workloads._bf16_codes(rng.standard_normal(shape).astype(np.float32))
+        v_new = workloads._bf16_codes(rng.standard_normal(shape).astype(np.float32))
+        q = workloads._bf16_codes(rng.standard_normal((w.batch, w.num_q_heads, w.head_size))
+                                  .astype(np.float32))
+        slots = np.concatenate([st.pool.append(st.tables[s], int(lens[s]), 1)[0]
+                                for s in range(w.batch)])
+        st.block_tables.copy_(torch.from_numpy(st.tables))
+        L.paged_kv_write(st.cache, torch.from_numpy(k_new.view(np.int16)).cuda(),
+                         torch.from_numpy(v_new.view(np.int16)).cuda(),
+                         torch.from_numpy(slots).cuda())
+        lens += 1
+        st.seq_lens.copy_(torch.from_numpy(lens))
+        st.q.copy_(torch.from_numpy(q.view(np.int16)))
+        st.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        out = st.out.cpu().numpy()
+        want = []
+        for s in range(w.batch):
+            Ks[s] = np.concatenate([Ks[s], k_new[s:s + 1]])
+            Vs[s] = np.concatenate([Vs[s], v_new[s:s + 1]])
+            want.append(po.attention_rows(po.decode(q[s:s + 1], "bf16"), po.decode(Ks[s], "bf16"),
+                                          po.decode(Vs[s], "bf16"), [int(lens[s]) - 1], w.scale))
+        _check_attention(out, np.concatenate(want), "bf16", f"replay after growth step {step}")
+
+
+@pytest.mark.parametrize("cfg", [5, 4])
+def test_debug_validate_mode_accepts_valid_calls(cfg, monkeypatch):
+    """PKV_DEBUG_VALIDATE=1 copies slots, copy pairs, tables and lengths to
+    the host and checks them before each launch; on valid steps (copies,
+    writes, mixed attention) the results are bit for bit those of the normal
+    mode."""
+    w = workloads.small(cfg)
+    _announce(f"debug-validate mode, small {w.name}")
+    plain = gpu_step.run_workload(w)
+    monkeypatch.setenv("PKV_DEBUG_VALIDATE", "1")
+    checked = gpu_step.run_workload(w)
+    assert np.array_equal(plain.pool_codes(), checked.pool_codes())
+    assert torch.equal(plain.out, checked.out)

@@ -298,3 +298,90 @@ def test_prefix_cache_replay_matches_oracle(seed):
         assert lib.num_free() == len(ora.free)
         assert [lib.refcnt(b) for b in range(nb)] == ora.ref
     assert total_hits > 50
+
+
+# ----------------------------------------- debug checks of device-side preconditions
+def _status(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+        return 0, ""
+    except L.PkvError as e:
+        return e.status, str(e)
+
+
+def test_layout_constant():
+    """The pool layout is exported as a value callers can check."""
+    assert P.pkv_layout() == P.PKV_LAYOUT_HEAD_KV_GRANULE16 == 1
+    assert "PKV_LAYOUT_HEAD_KV_GRANULE16 = 1" in open(os.path.join(ROOT, "include", "pkv.h")).read()
+
+
+def test_validate_slots_rejects_each_violation():
+    """paged_kv_write's preconditions (vLLM 源码精读 5.1: every new token has a
+    slot of its own): slots below num_blocks * 16, no slot written twice;
+    negative slots are skipped."""
+    d = P.descriptor(4, 2, 64, P.PKV_BF16)                # 64 slots
+    assert _status(P.pkv_validate_slots, d, [0, 63, -1, 17, -5, 16]) == (0, "")
+    assert _status(P.pkv_validate_slots, d, [])[0] == 0
+    st, msg = _status(P.pkv_validate_slots, d, [3, 64])
+    assert st == 7 and "slot_mapping[1] = 64" in msg
+    st, msg = _status(P.pkv_validate_slots, d, [3, 5, -1, 3])
+    assert st == 7 and "slot 3 is written by tokens 0 and 3" in msg
+    assert _status(P.pkv_validate_slots, P.descriptor(4, 2, 96, P.PKV_BF16), [0])[0] == 2
+
+
+def test_validate_block_pairs_rejects_each_violation():
+    """block_copy's preconditions (juhe.plus 3.8: copy-on-write copies a
+    shared block into a fresh one) and block_swap's (ids on both sides)."""
+    ok = [[0, 5], [0, 6], [1, 7]]                          # a source may repeat
+    assert _status(P.pkv_validate_block_pairs, ok, 8, 8, True)[0] == 0
+    for pairs, what in (([[8, 1]], "source block 8"), ([[-1, 1]], "source block -1"),
+                        ([[0, 8]], "destination block 8"), ([[0, 5], [1, 5]], "block 5 is the destination of pairs 0 and 1"),
+                        ([[0, 5], [5, 6]], "block 5 is the destination of pair 0 and the source of pair 1")):
+        st, msg = _status(P.pkv_validate_block_pairs, pairs, 8, 8, True)
+        assert st == 7 and what in msg, (pairs, msg)
+    # swap: two pools, so a block id may appear on both sides
+    assert _status(P.pkv_validate_block_pairs, [[0, 5], [5, 6]], 8, 8, False)[0] == 0
+    assert _status(P.pkv_validate_block_pairs, [[2, 9]], 3, 10, False)[0] == 0
+    assert _status(P.pkv_validate_block_pairs, [[3, 0]], 3, 10, False)[0] == 7
+    assert _status(P.pkv_validate_block_pairs, [[0, 10]], 3, 10, False)[0] == 7
+
+
+def test_validate_attention_rejects_each_violation():
+    """Attention's preconditions (juhe.plus 3.3 / 3.6: every position below
+    the length translates through a valid table entry)."""
+    d = P.descriptor(10, 2, 64, P.PKV_BF16)
+    bt = np.array([[3, 9, 0], [1, -1, -1]], np.int32)      # unused entries may hold anything
+    lens = np.array([33, 16], np.int32)
+    assert _status(P.pkv_validate_attention, d, bt, lens, lens)[0] == 0
+    assert _status(P.pkv_validate_attention, d, bt, lens, None, [0, 1, 2], [0, 1, 2])[0] == 0
+    assert _status(P.pkv_validate_attention, d, bt, [0, 0], [0, 0])[0] == 0
+    cases = [
+        (dict(seq_lens=[49, 16], h_seq_lens=None), "seq_lens[0] = 49 outside"),
+        (dict(seq_lens=[-1, 16], h_seq_lens=None), "seq_lens[0] = -1 outside"),
+        (dict(block_tables=[[3, 10, 0], [1, 0, 0]]), "block_tables[0][1] = 10"),
+        (dict(block_tables=[[3, 9, 0], [-1, 0, 0]]), "block_tables[1][0] = -1"),
+        (dict(seq_lens=[33, 17], h_seq_lens=None), "block_tables[1][1] = -1"),
+        (dict(h_seq_lens=[33, 15]), "seq_lens[1] = 16, but 15 in the host copy"),
+        (dict(query_start_loc=[0, 2, 3], h_query_start_loc=[0, 1, 3]), "query_start_loc[1] = 2"),
+        (dict(query_start_loc=[0, 34, 35], h_query_start_loc=None), "34 query rows and length 33"),
+        (dict(query_start_loc=[1, 2, 3], h_query_start_loc=None), "query_start_loc[0] = 1"),
+    ]
+    for change, what in cases:
+        kw = dict(block_tables=bt, seq_lens=lens, h_seq_lens=lens, query_start_loc=None,
+                  h_query_start_loc=None)
+        kw.update(change)
+        st, msg = _status(P.pkv_validate_attention, d, **kw)
+        assert st == 7 and what in msg, (change, msg)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_validators_accept_the_full_size_workloads(cfg):
+    """The tables, lengths, slots and copy-on-write pairs the library's
+    allocator builds for every full-size workload meet every precondition."""
+    w = workloads.make(cfg, values=False)
+    _, tables, slots, cows, _ = _gpu_side_tables(w)
+    d = P.descriptor(w.num_blocks, w.num_kv_heads, w.head_size, P.PKV_BF16)
+    P.pkv_validate_slots(d, slots)
+    P.pkv_validate_block_pairs(cows, w.num_blocks, w.num_blocks, True)
+    P.pkv_validate_attention(d, tables, w.seq_lens, w.seq_lens, w.query_start_loc,
+                             w.query_start_loc)
