@@ -216,6 +216,30 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q,
                            const int32_t* h_seq_lens, int32_t num_seqs, float scale,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* paged_attention_decode without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory around the
+ * call: code recorded under graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as
+ * paged_attention_decode (with the same kernels), except:
+ *  - the split rows' partials and counters live in a scratch array of
+ *    32 MiB that the library's code object holds on each device it runs on
+ *    until the process ends; a call whose partials (2 per wave of
+ *    num_q_heads / num_kv_heads rows of head_size + 2 floats) and counters
+ *    (8 bytes per sequence and kv head) do not fit returns PKV_ERR_WORKSPACE
+ *    before launching anything (about 250,000 sequences x kv heads at the
+ *    8B shape);
+ *  - every call on a device shares that device's array, so calls that may
+ *    overlap on one device (several streams, several host threads) race and
+ *    must be serialised by the caller;
+ *  - PKV_DECODE_SPLIT is ignored (the stream kernel always runs).
+ * Nothing in the array needs clearing between calls: split rows count their
+ * contributors in counters tagged with each call's own epoch. */
+int paged_attention_decode_noalloc(const pkv_cache* cache, float* out, const void* q,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   const int32_t* h_seq_lens, int32_t num_seqs, float scale,
+                                   void* stream);
+
 /* Mixed step: chunked-prefill rows and decode rows in one flattened batch
  * (Inside vLLM, "Forward pass" and "Chunked prefill"; juhe.plus section
  * 4.2).  Sequence s owns query rows query_start_loc[s] ..

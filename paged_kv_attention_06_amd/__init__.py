@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     block_swap,
     descriptor,
     paged_attention_decode,
+    paged_attention_decode_noalloc,
     paged_attention_mixed,
     paged_kv_write,
     pkv_attention_workspace_bytes,

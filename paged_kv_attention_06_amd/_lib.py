@@ -84,6 +84,10 @@ _c["pkv_pool_match_prefix"] = _sig("pkv_pool_match_prefix", ctypes.c_int,
 _c["pkv_pool_cache_blocks"] = _sig("pkv_pool_cache_blocks", ctypes.c_int,
                                    [_vp, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32])
 
+_c["paged_attention_decode_noalloc"] = _sig("paged_attention_decode_noalloc", ctypes.c_int,
+                                            [ctypes.POINTER(PkvCache), _vp, _vp, ctypes.c_int32,
+                                             _vp, ctypes.c_int32, _vp, _i32p, ctypes.c_int32,
+                                             ctypes.c_float, _vp])
 _c["pkv_layout"] = _sig("pkv_layout", ctypes.c_int, [])
 _c["pkv_validate_slots"] = _sig("pkv_validate_slots", ctypes.c_int,
                                 [ctypes.POINTER(PkvCache), _i64p, ctypes.c_int64])
@@ -267,6 +271,18 @@ def paged_attention_decode(cache: Cache, out, q, block_tables, seq_lens, h_seq_l
                                         _ptr_i32(hsl), hsl.shape[0], float(scale),
                                         _dev(workspace, "workspace"), ws_bytes, _stream(stream)),
            "paged_attention_decode")
+
+
+def paged_attention_decode_noalloc(cache: Cache, out, q, block_tables, seq_lens, h_seq_lens,
+                                   scale: float, stream=None) -> None:
+    hsl = _host_i32(h_seq_lens)
+    _check(_c["paged_attention_decode_noalloc"](cache.ref, _dev(out, "out"), _dev(q, "q"),
+                                                int(q.shape[1]),
+                                                _dev(block_tables, "block_tables"),
+                                                int(block_tables.shape[1]),
+                                                _dev(seq_lens, "seq_lens"), _ptr_i32(hsl),
+                                                hsl.shape[0], float(scale), _stream(stream)),
+           "paged_attention_decode_noalloc")
 
 
 def paged_attention_mixed(cache: Cache, out, q, query_start_loc, seq_lens, h_query_start_loc,

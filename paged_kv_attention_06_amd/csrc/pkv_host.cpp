@@ -251,16 +251,21 @@ struct WsLayout {
   size_t v_off, exp_off, total;
   size_t st_ml_off, st_ctr_off;  // stream layout (offsets from the start)
 };
-WsLayout ws_layout(const Plan& p, int hq, int hkv, int D) {
+// stream_waves >= 0 sizes the stream region for that many waves and leaves
+// out the fixed partitions' region (the no-allocation entry point, which
+// always takes the stream kernel); otherwise both paths fit, for the most
+// waves any device may launch.
+WsLayout ws_layout(const Plan& p, int hq, int hkv, int D, int64_t stream_waves = -1) {
   WsLayout w{0, 0, 0, 0, 0};
   size_t dec_end = pkv::kWorkspaceHeader;
   if (p.decode_units > 0) {
     const int G = hq / hkv;
-    const size_t wc = (size_t)stream_wave_cap(p, hkv);
+    const size_t wc = (size_t)(stream_waves >= 0 ? stream_waves : stream_wave_cap(p, hkv));
     w.st_ml_off = pkv::kWorkspaceHeader + 2 * wc * G * D * sizeof(float);
     w.st_ctr_off = (w.st_ml_off + 2 * wc * G * 2 * sizeof(float) + 255) / 256 * 256;
     const size_t st_total = w.st_ctr_off + (size_t)p.num_seqs * hkv * 8;
-    const size_t units = pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
+    const size_t units = stream_waves >= 0 ? 0
+        : pkv::kWorkspaceHeader + (size_t)p.decode_units * hq * (D + 2) * sizeof(float);
     dec_end = st_total > units ? st_total : units;
   }
   if (p.prefill_vblocks == 0) {
@@ -278,7 +283,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
               const int32_t* qsl, const int32_t* seq_lens, const int32_t* h_qsl,
               const int32_t* h_seq_lens, const int32_t* block_tables, int32_t max_blocks,
               int32_t num_seqs, int64_t num_tokens, float scale, void* workspace,
-              size_t ws_bytes, void* stream, bool mixed) {
+              size_t ws_bytes, void* stream, bool mixed, bool noalloc = false) {
   pkv::CacheDesc c;
   if (int e = check_cache(cache, &c)) return e;
   if (num_q_heads < 1 || num_q_heads % c.hkv != 0)
@@ -304,8 +309,39 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   if (!out || !q || !seq_lens || !block_tables || (mixed && !qsl))
     return fail(PKV_ERR_NULL, "a device pointer (out, q, seq_lens, block_tables%s) is NULL",
                 mixed ? ", query_start_loc" : "");
-  const WsLayout wl = ws_layout(plan, num_q_heads, c.hkv, c.head_size);
+  // Stream decode of the decode rows: how many waves.  A decode call whose
+  // rows are all empty still runs one wave, which writes their zero rows
+  // (and, replayed from a graph after the lengths grew, walks them).
+  const bool mixed_call = plan.prefill_tiles > 0 && plan.decode_units > 0;
+  const bool decode_rows = plan.decode_units > 0 || (!mixed && num_seqs > 0);
+  int64_t waves = 0;
+  bool stream_path = false;
+  if (decode_rows && (noalloc || stream_decode_enabled() || c.fp8) &&
+      (!mixed_call || mixed_concurrent_enabled())) {
+    const int G = num_q_heads / c.hkv;
+    // Beside prefill tiles the decode keeps one wave per SIMD: a SIMD then
+    // holds one prefill wave and one decode wave.
+    const int slots = mixed_call ? 4 * pkv::device_cus()
+                                 : pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
+    waves = stream_wave_cap(plan, c.hkv);
+    if (waves < 1) waves = 1;
+    if (slots > 0 && slots < waves) waves = slots;
+    if (const char* e = std::getenv("PKV_STREAM_WAVES")) {  // tuning: cap the waves
+      const long long cap = std::atoll(e);
+      if (cap > 0 && cap < waves) waves = cap;
+    }
+    stream_path = slots > 0;
+  }
+  if (noalloc && !stream_path)
+    return fail(PKV_ERR_HIP, "the no-allocation decode needs the device's wave count");
+  const WsLayout wl = noalloc ? ws_layout(plan, num_q_heads, c.hkv, c.head_size, waves)
+                              : ws_layout(plan, num_q_heads, c.hkv, c.head_size);
   const size_t need = wl.total;
+  if (noalloc && need > ws_bytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                "(%d sequences x %d kv heads, %lld waves)",
+                need, ws_bytes, num_seqs, c.hkv, (long long)waves);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
   if (debug_validate()) {
@@ -350,42 +386,22 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   a.stream_waves = 0;
   a.stream_rounds = 0;
-  const bool mixed_call = plan.prefill_tiles > 0 && plan.decode_units > 0;
-  // A decode call whose rows are all empty still runs one stream wave, which
-  // writes their zero rows (and, replayed from a graph after the lengths
-  // grew, walks them).
-  const bool decode_rows = plan.decode_units > 0 || (!mixed && num_seqs > 0);
-  if (decode_rows && (stream_decode_enabled() || c.fp8) &&
-      (!mixed_call || mixed_concurrent_enabled())) {
-    const int G = num_q_heads / c.hkv;
-    // Beside prefill tiles the decode keeps one wave per SIMD: a SIMD then
-    // holds one prefill wave and one decode wave.
-    const int slots = mixed_call ? 4 * pkv::device_cus()
-                                 : pkv::decode_stream_slots(c.dtype_bytes, c.head_size, G);
-    int64_t waves = stream_wave_cap(plan, c.hkv);
-    if (waves < 1) waves = 1;
-    if (slots > 0 && slots < waves) waves = slots;
-    if (const char* e = std::getenv("PKV_STREAM_WAVES")) {  // tuning: cap the waves
-      const long long cap = std::atoll(e);
-      if (cap > 0 && cap < waves) waves = cap;
-    }
-    if (slots > 0) {
-      static std::atomic<unsigned> epoch{first_epoch()};
-      a.stream_waves = (int)waves;
-      a.stream_c0 = pkv::kStreamSetupCost;
-      a.stream_epoch = epoch.fetch_add(2, std::memory_order_relaxed);
-      // waves per SIMD (rounds of dispatch), which rotate their priority;
-      // beside prefill tiles there is one decode wave per SIMD: off
-      const int simds = 4 * pkv::device_cus();
-      const int64_t rounds = simds > 0 ? (waves + simds - 1) / simds : 0;
-      a.stream_rounds = (!mixed_call && rounds > 1) ? (int)(rounds < 4 ? rounds : 4) : 0;
-      // (no decode region when every row is empty: one wave, nothing split)
-      const bool region = ws && plan.decode_units > 0;
-      a.stream_acc = region ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;
-      a.stream_ml = region ? reinterpret_cast<float*>(ws + wl.st_ml_off) : nullptr;
-      a.stream_counters =
-          region ? reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off) : nullptr;
-    }
+  if (stream_path) {
+    static std::atomic<unsigned> epoch{first_epoch()};
+    a.stream_waves = (int)waves;
+    a.stream_c0 = pkv::kStreamSetupCost;
+    a.stream_epoch = epoch.fetch_add(2, std::memory_order_relaxed);
+    // waves per SIMD (rounds of dispatch), which rotate their priority;
+    // beside prefill tiles there is one decode wave per SIMD: off
+    const int simds = 4 * pkv::device_cus();
+    const int64_t rounds = simds > 0 ? (waves + simds - 1) / simds : 0;
+    a.stream_rounds = (!mixed_call && rounds > 1) ? (int)(rounds < 4 ? rounds : 4) : 0;
+    // (no decode region when every row is empty: one wave, nothing split)
+    const bool region = ws && plan.decode_units > 0;
+    a.stream_acc = region ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;
+    a.stream_ml = region ? reinterpret_cast<float*>(ws + wl.st_ml_off) : nullptr;
+    a.stream_counters =
+        region ? reinterpret_cast<unsigned long long*>(ws + wl.st_ctr_off) : nullptr;
   }
   if (c.fp8 && decode_rows && a.stream_waves == 0)
     return fail(PKV_ERR_HIP, "fp8 decode needs the device's wave count (hipGetDevice failed)");
@@ -539,6 +555,19 @@ int paged_attention_decode(const pkv_cache* cache, float* out, const void* q, in
   return attention(cache, out, q, num_q_heads, nullptr, seq_lens, nullptr, h_seq_lens,
                    block_tables, max_blocks_per_seq, num_seqs, num_seqs, scale, workspace,
                    workspace_bytes, stream, false);
+}
+
+int paged_attention_decode_noalloc(const pkv_cache* cache, float* out, const void* q,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   const int32_t* h_seq_lens, int32_t num_seqs, float scale,
+                                   void* stream) {
+  char* scratch = nullptr;
+  if (hipError_t e = pkv::noalloc_scratch(&scratch))
+    return fail(PKV_ERR_HIP, "scratch address (hipGetSymbolAddress): %s", hipGetErrorString(e));
+  return attention(cache, out, q, num_q_heads, nullptr, seq_lens, nullptr, h_seq_lens,
+                   block_tables, max_blocks_per_seq, num_seqs, num_seqs, scale, scratch,
+                   pkv::kNoAllocScratchBytes, stream, false, true);
 }
 
 int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q, int32_t num_q_heads,

@@ -95,6 +95,12 @@ hipError_t launch_prefill_rows(const CacheDesc& c, const AttnDesc& a, hipStream_
 // share the GPU, then the merge of split decode rows.
 hipError_t launch_mixed_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);
 
+// Bytes of the scratch array of paged_attention_decode_noalloc (one per
+// device), and its device address on the current device (looked up once per
+// device; the array's name is not usable as an address in host code).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(char** ptr);
+
 bool supported_group(int g);
 // Waves of the stream decode kernel the current device holds at once (0 if
 // it cannot be queried).

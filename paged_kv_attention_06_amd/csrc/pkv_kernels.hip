@@ -2842,6 +2842,38 @@ static SideStream* side_stream(hipError_t* err) {
   return ss.err == hipSuccess ? &ss : nullptr;
 }
 
+// Scratch of paged_attention_decode_noalloc: the stream decode's partials
+// and counters in a fixed array of device memory that the code object holds
+// on every device it runs on, until the process ends, so that entry point
+// allocates nothing.  In host code the array's name is not its device
+// address: the address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address reaches a kernel.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+struct ScratchAddr {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  char* ptr = nullptr;
+};
+static ScratchAddr g_scratch[kMaxDevices];
+
+hipError_t noalloc_scratch(char** ptr) {
+  *ptr = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchAddr& sa = g_scratch[dev];
+  std::call_once(sa.once, [&sa]() {
+    void* addr = nullptr;
+    sa.err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (sa.err == hipSuccess && !addr) sa.err = hipErrorInvalidSymbol;
+    if (sa.err == hipSuccess) sa.ptr = static_cast<char*>(addr);
+  });
+  *ptr = sa.ptr;
+  return sa.err;
+}
+
 // Prefill tiles (HBM-light, MFMA-bound) and decode rows (HBM-bound) of one
 // mixed call side by side: the fp16 copy of V and then the tiles on the
 // side stream, the stream decode on the caller's.  The tile kernel gets ~81
