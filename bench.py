@@ -10,7 +10,14 @@ HBM before timing starts.
 Prints one JSON line (rank 0, N = 1).  The roofline object describes the
 attention call, the dominant cost of the step: algorithmic bytes (every
 valid token's K and V once, plus q, out, tables and lengths) divided by its
-average duration from HIP events on the launch stream.
+average duration from HIP events on the launch stream.  Beside it, each with
+its own roofline: `gather_ceiling` (the same batch's (block, kv head) slices
+read once by pkv_read_slices, no arithmetic: the read rate this access
+pattern allows), `mixed_step` (the 8B GQA chunked-prefill step: 98 decode
+rows plus a 1950-row chunk, against the serialized HBM + MFMA bound) and
+`prefill_chunk` (that chunk alone, against the bf16 MFMA peak).  The CPU
+baseline (the oracle on every host core) runs first, before the GPU is
+touched.
 """
 from __future__ import annotations
 
@@ -27,18 +34,24 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
-# HBM bytes one attention call moves on this workload, from rocprofv3
-# FETCH_SIZE (scaled by the factor a 1 GiB device copy needs) plus WRITE_SIZE
-# of k_decode_stream (2048 waves); see profiles/decode_8b_gqa_b256_traffic.md.
-# Reset to None whenever the kernel or its launch changes until the counters
-# are taken again.
-MEASURED_TRAFFIC_BYTES = 1_367_751_000
-# The same for the FP8 E4M3 cache variant (k_decode_stream<1,128,4>, 3072
-# waves); see profiles/decode_8b_gqa_b256_fp8_kv.md.
-MEASURED_TRAFFIC_BYTES_FP8 = 701_345_000
-# The same for the speculative-verify batch (k_prefill_mq<128,4>); see
-# profiles/verify_8b_gqa_b256_k3_multi_query.md.
-MEASURED_TRAFFIC_BYTES_VERIFY = 1_486_721_000
+# HBM bytes per launch of the dominant kernel of each workload, from two
+# rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each scaled by what the
+# counter reads for a device copy of known size), with the SHA-256 of the
+# kernel source they were taken on (profiles/traffic.json).  A figure is
+# reported only while the kernel source is unchanged; otherwise `traffic` is
+# null until the counters are taken again.
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_attention_06_amd", "csrc", "pkv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def measured_traffic(key: str):
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[key]
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    return int(rec["bytes_per_launch"]) if rec.get("kernel_source_sha256") == sha else None
 
 
 def algorithmic_kv_bytes(w) -> int:
@@ -72,26 +85,77 @@ def unique_kv_bytes(w, tables) -> int:
     return sum(used.values()) * 2 * w.num_kv_heads * w.head_size * w.kv_dtype_bytes
 
 
-def cpu_baseline(w, min_s: float = 10.0):
-    """The oracle (unchanged) on the host: textbook fp64 attention of whole
-    decode rows, one sequence at a time, single-threaded BLAS, repeated over
-    the batch until at least ``min_s`` seconds of work are done."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(rows, dtype, scale, seconds, ready, start, out):
+    """Worker of the CPU baseline: its share of decode rows arrives with the
+    process; after every worker is ready it computes the oracle's rows over
+    and over with one BLAS thread for `seconds` and reports the rows done."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import scenario
-    order = np.random.default_rng(1).permutation(w.batch)
-    done_rows = 0
-    t0 = time.perf_counter()
+    from oracle import paged_oracle as po
+    done = 0
     with threadpool_limits(1):
-        while time.perf_counter() - t0 < min_s:
-            for s in order:
-                scenario.sequence_attention(w, int(s))
-                done_rows += 1
-    dt = time.perf_counter() - t0
-    return {"value": done_rows / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_rows} decode rows ({done_rows / w.batch:.0f} passes over the "
-                      f"{w.batch}-row batch, all {w.num_q_heads} heads each), fp64 NumPy, "
-                      f"1 thread, {dt:.1f} s"}
+        ready.put(1)
+        start.wait()
+        deadline = time.time() + seconds
+        while time.time() < deadline:
+            for q, K, V, L in rows:
+                po.attention_rows(po.decode(q, dtype), po.decode(K, dtype), po.decode(V, dtype),
+                                  [L - 1], scale)
+                done += 1
+                if time.time() >= deadline:
+                    break
+    out.put(done)
+
+
+def cpu_baseline(w, seconds: float = 12.0):
+    """The oracle (unchanged) on every host core, before the GPU is touched:
+    one spawned worker process per core with one BLAS thread, each given its
+    share of the batch's decode rows (query codes and the sequence's K/V
+    codes in logical order, dealt round-robin in a seeded random order) and
+    computing textbook fp64 attention of those rows, all heads, over and
+    over for a fixed wall time that starts once every worker holds its data.
+    The rate is rows per second over all workers."""
+    import multiprocessing as mp
+
+    from oracle import scenario
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    workers = max(1, min(cores, 32))
+    order = np.random.default_rng(1).permutation(w.batch)
+    qsl = w.query_start_loc
+    shares = [[] for _ in range(workers)]
+    for i, s in enumerate(order):
+        K, V = scenario.sequence_kv(w, int(s))
+        shares[i % workers].append((w.q[qsl[s]:qsl[s] + 1], K, V, int(w.seq_lens[s])))
+    ctx = mp.get_context("spawn")
+    ready, out, start = ctx.Queue(), ctx.Queue(), ctx.Event()
+    procs = [ctx.Process(target=_oracle_worker,
+                         args=(sh, w.dtype, w.scale, seconds, ready, start, out))
+             for sh in shares]
+    for pr in procs:
+        pr.start()
+    for _ in procs:
+        ready.get(timeout=600)
+    t0 = time.time()
+    start.set()
+    rows = sum(out.get(timeout=600 + seconds) for _ in procs)
+    dt = time.time() - t0
+    for pr in procs:
+        pr.join()
+    return {"value": rows / dt, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(), "host_cores": os.cpu_count(),
+            "sample": f"{rows} decode rows of this batch (all {w.num_q_heads} heads each) in "
+                      f"{dt:.1f} s on {workers} worker processes, fp64 NumPy, one BLAS thread "
+                      f"each"}
 
 
 def prefill_flops(w) -> float:
@@ -151,9 +215,13 @@ def copy_bandwidth(nbytes=1 << 30):
     return 2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9
 
 
-def run_mixed(args):
-    """The 8B GQA mixed step (98 decode rows + a 1950-row chunk): the whole
-    mixed call, and the prefill chunk alone."""
+MFMA_PEAK_TFLOPS = 2500.0  # bf16 dense
+
+
+def measure_mixed(steps: int, warmup: int, flush_mb: int):
+    """The 8B GQA mixed step (98 decode rows + a 1950-row chunk on 1048 cached
+    tokens): the whole mixed call, and the chunk's rows alone through the
+    same entry point.  Returns (mixed_step, prefill_chunk) records."""
     import torch
 
     import workloads
@@ -167,8 +235,8 @@ def run_mixed(args):
     st.run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    flush = make_flush(args.flush_mb)
-    mixed_ms = _timed(st.attend, args.steps, args.warmup, stream, flush)
+    flush = make_flush(flush_mb)
+    mixed_ms = _timed(st.attend, steps, warmup, stream, flush)
     # the chunk alone: same call restricted to the prefill sequence
     s = int(np.argmax(w.q_len))
     r0, r1 = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
@@ -186,7 +254,7 @@ def run_mixed(args):
         L.paged_attention_mixed(st.cache, out, q, d_qsl, d_len, sub_qsl, sub_len, d_bt, w.scale,
                                 ws)
 
-    pre_ms = _timed(prefill, args.steps, args.warmup, stream, flush)
+    pre_ms = _timed(prefill, steps, warmup, stream, flush)
     torch.cuda.synchronize()
     # The mixed call runs the chunk in 4-wave workgroups beside the decode
     # rows; alone it may split each q tile's keys over two groups, which
@@ -203,23 +271,93 @@ def run_mixed(args):
     pre_mean = float(pre_ms.mean())
     tflops = flops / (pre_mean * 1e-3) / 1e12
     mixed_mean = float(mixed_ms.mean())
+    # bytes the whole call must move (every sequence's K/V once, q, out,
+    # tables, lengths, query_start_loc) and those of the decode rows alone
+    all_bytes = algorithmic_bytes(w)
+    dec = np.flatnonzero(w.q_len == 1)
+    dec_bytes = (int(w.seq_lens[dec].astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * 2
+                 + len(dec) * w.num_q_heads * w.head_size * (2 + 4)
+                 + int(((w.seq_lens[dec].astype(np.int64) + 15) // 16).sum()) * 4 + 4 * len(dec))
+    bound_ms = all_bytes / (HBM_PEAK_GBPS * 1e9) * 1e3 + flops / (MFMA_PEAK_TFLOPS * 1e12) * 1e3
+    mixed_rec = {
+        "ms": mixed_mean,
+        "ms_median_p10_p90": [float(np.median(mixed_ms)), float(np.percentile(mixed_ms, 10)),
+                              float(np.percentile(mixed_ms, 90))],
+        "workload": "8B GQA mixed step: 98 decode rows (contexts U[64,4096]) + one 1950-token "
+                    "prefill chunk on 1048 cached tokens, 2048 new tokens",
+        "roofline": {"bound": "hbm+mfma (serialized)", "achieved_ms": mixed_mean,
+                     "bound_ms": bound_ms, "frac": bound_ms / mixed_mean,
+                     "algorithmic_bytes": all_bytes, "algorithmic_flops": flops,
+                     "peaks": {"hbm_GBps": HBM_PEAK_GBPS, "mfma_TFLOPs": MFMA_PEAK_TFLOPS},
+                     "traffic": None},
+        "decode_rows_bytes": dec_bytes,
+        "decode_rows_pct_hbm_peak_over_the_call": 100.0 * dec_bytes / (mixed_mean * 1e-3) / 1e9
+        / HBM_PEAK_GBPS,
+        "kernels": "k_v_fp16 + k_prefill_tile on the side stream beside k_decode_stream",
+    }
+    prefill_rec = {
+        "ms": pre_mean,
+        "ms_median_p10_p90": [float(np.median(pre_ms)), float(np.percentile(pre_ms, 10)),
+                              float(np.percentile(pre_ms, 90))],
+        "workload": "the mixed step's 1950-row chunk alone (1048 cached tokens, causal), 8B GQA",
+        "gflop": flops / 1e9,
+        "alone_vs_mixed_max_abs": alone_vs_mixed,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "k_v_fp16 + " + chunk_kernel,
+                     "algorithmic_flops_per_launch": flops},
+    }
+    del st
+    return mixed_rec, prefill_rec
+
+
+def measure_gather(st, w, steps: int, warmup: int, flush_mb: int, decode_ms: float):
+    """The read ceiling of the decode batch's access pattern: pkv_read_slices
+    over the (block, kv head) slices the decode reads, in its order
+    (sequence, kv head, block), with as many waves as the decode and the same
+    1 GiB read before every call."""
+    import torch
+
+    from paged_kv_attention_06_amd import _lib as L
+    ids = []
+    for s in range(w.batch):
+        nb = -(-int(w.seq_lens[s]) // 16)
+        row = st.tables[s][:nb].astype(np.int64) * w.num_kv_heads
+        for h in range(w.num_kv_heads):
+            ids.append(row + h)
+    ids = torch.from_numpy(np.concatenate(ids)).cuda()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = 8 * cus
+    sink = torch.empty(waves, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ms = _timed(lambda: L.pkv_read_slices(st.cache, ids, waves, sink), steps, warmup, stream,
+                make_flush(flush_mb))
+    ms_b2b = _timed(lambda: L.pkv_read_slices(st.cache, ids, waves, sink), steps, warmup, stream)
+    slice_bytes = 2 * 16 * w.head_size * w.kv_dtype_bytes
+    nbytes = int(ids.shape[0]) * slice_bytes
+    mean = float(ms.mean())
+    gbps = nbytes / (mean * 1e-3) / 1e9
+    return {
+        "ms": mean, "ms_back_to_back": float(ms_b2b.mean()),
+        "bytes_read": nbytes, "slices": int(ids.shape[0]), "waves": waves,
+        "gbps": gbps, "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "gbps_back_to_back": nbytes / (float(ms_b2b.mean()) * 1e-3) / 1e9,
+        "decode_call_vs_probe_time": decode_ms / mean,
+        "kernel": "pkv_read_slices (k_read_slices): the decode's slices read once, no arithmetic",
+    }
+
+
+def run_mixed(args):
+    mixed, prefill = measure_mixed(args.steps, args.warmup, args.flush_mb)
     return {
         "metric": "mixed chunked-prefill step: attention ms and prefill-tile MFMA TFLOP/s",
-        "value": mixed_mean, "unit": "ms", "higher_is_better": False,
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed_mean,
+        "value": mixed["ms"], "unit": "ms", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed["ms"],
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "8B GQA mixed step: 98 decode rows (contexts U[64,4096]) + one "
-                               "1950-token prefill chunk on 1048 cached tokens, 2048 new tokens",
+        "config": {"workload": mixed["workload"],
                    "flush_mb_read_before_each_step": args.flush_mb},
-        "prefill_ms": pre_mean,
-        "prefill_ms_median_p10_p90": [float(np.median(pre_ms)), float(np.percentile(pre_ms, 10)),
-                                      float(np.percentile(pre_ms, 90))],
-        "prefill_gflop": flops / 1e9,
-        "prefill_alone_vs_mixed_max_abs": alone_vs_mixed,
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": tflops / 2500.0, "traffic": None,
-                     "kernel": "the chunk's rows alone: k_v_fp16 + " + chunk_kernel,
-                     "algorithmic_flops_per_launch": flops},
+        "mixed_step": mixed, "prefill_chunk": prefill,
+        "roofline": prefill["roofline"],
     }
 
 
@@ -385,6 +523,8 @@ def main() -> None:
                          "sequence (speculative decoding); all but decode are reported "
                          "separately")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode workload: skip the read ceiling, mixed step and prefill chunk")
     ap.add_argument("--chunk-rows", type=int, default=512,
                     help="prefill workload: query rows of the chunk")
     ap.add_argument("--cached", type=int, default=1048,
@@ -401,15 +541,33 @@ def main() -> None:
         print(json.dumps(run_prefix_cache(args)), flush=True)
         return
 
-    import torch
-
     import workloads
-    from paged_kv_attention_06_amd import step as gpu_step
 
     lib = os.path.join(ROOT, "paged_kv_attention_06_amd", "libpkv.so")
     if not os.path.exists(lib):
         import __graft_entry__
         __graft_entry__.build()
+
+    fp8 = args.workload == "decode-fp8"
+    verify = args.workload == "verify"
+    other = {"decode-7b": 2, "decode-13b": 5, "tiny": 1}.get(args.workload)
+    headline = args.workload == "decode"
+    w = None
+    cpu = None
+    if args.workload not in ("mixed", "swap", "prefill"):
+        if fp8:
+            w = workloads.make_fp8(3)
+        elif verify:
+            w = workloads.make_verify()
+        else:
+            w = workloads.make(other or 3)
+        # the oracle on the host cores, before anything touches the GPU
+        if headline and not args.no_cpu_baseline:
+            cpu = cpu_baseline(w)
+
+    import torch
+
+    from paged_kv_attention_06_amd import step as gpu_step
 
     if args.workload == "mixed":
         print(json.dumps(run_mixed(args)), flush=True)
@@ -421,15 +579,6 @@ def main() -> None:
         print(json.dumps(run_prefill(args)), flush=True)
         return
 
-    fp8 = args.workload == "decode-fp8"
-    verify = args.workload == "verify"
-    other = {"decode-7b": 2, "decode-13b": 5, "tiny": 1}.get(args.workload)
-    if fp8:
-        w = workloads.make_fp8(3)
-    elif verify:
-        w = workloads.make_verify()
-    else:
-        w = workloads.make(other or 3)
     st = gpu_step.PagedStep(w, "cuda")
     st.build_history()
     st.prepare_step()
@@ -530,15 +679,24 @@ def main() -> None:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if other else (MEASURED_TRAFFIC_BYTES_VERIFY if verify else
-                                           MEASURED_TRAFFIC_BYTES_FP8 if fp8 else
-                                           MEASURED_TRAFFIC_BYTES),
+            "traffic": None if other else measured_traffic(
+                "verify_8b_gqa_b256_k3" if verify else
+                "decode_8b_gqa_b256_fp8" if fp8 else "decode_8b_gqa_b256"),
             "kernel": ("paged_attention_mixed (k_prefill_mq)" if verify else
                        "paged_attention_decode (k_decode_stream, one launch)"),
             "algorithmic_bytes_per_launch": alg,
         },
-        "cpu_baseline": None if (args.no_cpu_baseline or fp8 or verify or other) else cpu_baseline(w),
+        "cpu_baseline": cpu,
     }
+    if headline and not args.headline_only:
+        # beside the headline: the read ceiling of this batch's access
+        # pattern, then the mixed chunked-prefill step and its chunk alone
+        rec["gather_ceiling"] = measure_gather(st, w, args.steps, args.warmup, args.flush_mb,
+                                               attn_mean)
+        del st
+        torch.cuda.empty_cache()
+        rec["mixed_step"], rec["prefill_chunk"] = measure_mixed(args.steps, args.warmup,
+                                                                args.flush_mb)
     print(json.dumps(rec), flush=True)
 
 

@@ -268,6 +268,22 @@ int paged_attention_mixed(const pkv_cache* cache, float* out, const void* q,
                           int32_t max_blocks_per_seq, int32_t num_seqs, int64_t num_tokens,
                           float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ----------------------------------------------------------- measurement */
+/* The read rate the decode's access pattern allows on this device: every
+ * listed (block, kv head) slice of the pool -- its K and V tiles, 2 * 16 *
+ * head_size * dtype_bytes contiguous bytes -- is read once, with the loads
+ * the decode uses (1 KiB per instruction, two slices per step per wave with
+ * the next step in flight), by `waves` waves that take equal runs of the
+ * list; nothing is computed from the values but the XOR of every 32-bit
+ * word a wave read, which goes to sink[wave].  Timing this call over the
+ * slices a decode batch reads gives that batch's read ceiling.
+ *   slices  device int64 [num_slices], each block * num_kv_heads + kv head
+ *   sink    device uint32 [waves]
+ * Preconditions on device data: slice ids in [0, num_blocks * num_kv_heads)
+ * (checked under PKV_DEBUG_VALIDATE=1). */
+int pkv_read_slices(const pkv_cache* cache, const int64_t* slices, int64_t num_slices,
+                    int32_t waves, uint32_t* sink, void* stream);
+
 /* --------------------------------- preconditions on device data (debug) */
 /* Checks of the preconditions the calls above state on device data, run on
  * host copies of that data (PKV_DEBUG_VALIDATE=1 runs them inside the calls;

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     pkv_block_hash,
     pkv_build_slot_mapping,
     pkv_layout,
+    pkv_read_slices,
     pkv_validate_attention,
     pkv_validate_block_pairs,
     pkv_validate_slots,

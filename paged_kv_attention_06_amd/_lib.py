@@ -88,6 +88,9 @@ _c["paged_attention_decode_noalloc"] = _sig("paged_attention_decode_noalloc", ct
                                             [ctypes.POINTER(PkvCache), _vp, _vp, ctypes.c_int32,
                                              _vp, ctypes.c_int32, _vp, _i32p, ctypes.c_int32,
                                              ctypes.c_float, _vp])
+_c["pkv_read_slices"] = _sig("pkv_read_slices", ctypes.c_int,
+                             [ctypes.POINTER(PkvCache), _vp, ctypes.c_int64, ctypes.c_int32, _vp,
+                              _vp])
 _c["pkv_layout"] = _sig("pkv_layout", ctypes.c_int, [])
 _c["pkv_validate_slots"] = _sig("pkv_validate_slots", ctypes.c_int,
                                 [ctypes.POINTER(PkvCache), _i64p, ctypes.c_int64])
@@ -271,6 +274,14 @@ def paged_attention_decode(cache: Cache, out, q, block_tables, seq_lens, h_seq_l
                                         _ptr_i32(hsl), hsl.shape[0], float(scale),
                                         _dev(workspace, "workspace"), ws_bytes, _stream(stream)),
            "paged_attention_decode")
+
+
+def pkv_read_slices(cache: Cache, slices, waves: int, sink, stream=None) -> None:
+    """slices: int64 GPU tensor of block * num_kv_heads + kv head; sink: int32
+    GPU tensor of `waves` entries (the XOR of each wave's words)."""
+    _check(_c["pkv_read_slices"](cache.ref, _dev(slices, "slices"), int(slices.shape[0]),
+                                 int(waves), _dev(sink, "sink"), _stream(stream)),
+           "pkv_read_slices")
 
 
 def paged_attention_decode_noalloc(cache: Cache, out, q, block_tables, seq_lens, h_seq_lens,

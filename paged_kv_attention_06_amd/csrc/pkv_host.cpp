@@ -535,6 +535,26 @@ int block_swap(const pkv_cache* cache, void* host_kv, int64_t num_host_blocks,
                     "block_swap");
 }
 
+int pkv_read_slices(const pkv_cache* cache, const int64_t* slices, int64_t num_slices,
+                    int32_t waves, uint32_t* sink, void* stream) {
+  pkv::CacheDesc c;
+  if (int e = check_cache(cache, &c)) return e;
+  if (num_slices < 0 || waves < 1 || waves > (1 << 20))
+    return fail(PKV_ERR_DIM, "num_slices %lld, waves %d", (long long)num_slices, waves);
+  if (!sink || (num_slices > 0 && !slices)) return fail(PKV_ERR_NULL, "slices or sink is NULL");
+  if (debug_validate() && num_slices > 0) {
+    std::vector<int64_t> sv;
+    if (int e = fetch(sv, slices, (size_t)num_slices, stream, "slices")) return e;
+    for (int64_t i = 0; i < num_slices; ++i)
+      if (sv[(size_t)i] < 0 || sv[(size_t)i] >= c.num_blocks * c.hkv)
+        return fail(PKV_ERR_RANGE, "slices[%lld] = %lld outside [0, num_blocks * num_kv_heads)",
+                    (long long)i, (long long)sv[(size_t)i]);
+  }
+  return hip_status(pkv::launch_read_slices(c, slices, num_slices, waves, sink,
+                                            static_cast<hipStream_t>(stream)),
+                    "pkv_read_slices");
+}
+
 size_t pkv_attention_workspace_bytes(const pkv_cache* cache, int32_t num_q_heads,
                                      const int32_t* h_qsl, const int32_t* h_seq_lens,
                                      int32_t num_seqs) {

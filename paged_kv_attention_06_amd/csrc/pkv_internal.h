@@ -83,6 +83,9 @@ hipError_t launch_block_copy(const CacheDesc& c, const int64_t* pairs, int64_t n
 // Whole blocks between the device pool and a device-mapped host pool.
 hipError_t launch_block_swap(const CacheDesc& c, char* host_dev_ptr, const int64_t* pairs,
                              int64_t num_pairs, bool to_host, hipStream_t stream);
+// Read probe: every listed (block, kv head) slice once, XOR per wave.
+hipError_t launch_read_slices(const CacheDesc& c, const int64_t* slices, int64_t n, int waves,
+                              uint32_t* sink, hipStream_t stream);
 // Decode rows (one query row per sequence, or the q_len == 1 rows of a mixed
 // batch): split-K partition pass, then the merge of multi-partition rows.
 hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t stream);

@@ -710,3 +710,31 @@ def test_debug_validate_mode_accepts_valid_calls(cfg, monkeypatch):
     checked = gpu_step.run_workload(w)
     assert np.array_equal(plain.pool_codes(), checked.pool_codes())
     assert torch.equal(plain.out, checked.out)
+
+
+@pytest.mark.parametrize("waves", [1, 7, 300])
+def test_read_probe_checksums(waves):
+    """pkv_read_slices reads every listed (block, kv head) slice once: the
+    XOR of the 32-bit words each wave read equals the XOR of the same
+    slices of the pool computed on the host, for wave counts that leave
+    some waves idle and runs longer than one 64-slice id chunk."""
+    from paged_kv_attention_06_amd import _lib as L
+    w = workloads.small(3)
+    _announce(f"read probe, {waves} waves")
+    st = gpu_step.run_workload(w)
+    pool = st.pool_codes().view(np.uint32)            # [blocks][Hkv][2 * 16 * D / 2]
+    ids = [int(b) * w.num_kv_heads + h for s in range(w.batch) for h in range(w.num_kv_heads)
+           for b in st.tables[s][:-(-int(w.seq_lens[s]) // 16)]]
+    ids += ids[:5]                                    # a slice read twice is folded twice
+    sl = torch.tensor(ids, dtype=torch.int64, device="cuda")
+    sink = torch.full((waves,), -1, dtype=torch.int32, device="cuda")
+    L.pkv_read_slices(st.cache, sl, waves, sink)
+    torch.cuda.synchronize()
+    got = sink.cpu().numpy().view(np.uint32)
+    n = len(ids)
+    for wv in range(waves):
+        a, b = wv * n // waves, (wv + 1) * n // waves
+        x = np.uint32(0)
+        for i in ids[a:b]:
+            x ^= np.bitwise_xor.reduce(pool[i // w.num_kv_heads, i % w.num_kv_heads].reshape(-1))
+        assert got[wv] == x, f"wave {wv} of {waves}"
