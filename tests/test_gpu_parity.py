@@ -650,7 +650,8 @@ def test_graph_replay_follows_growing_lengths():
     library's allocator (new blocks enter the same table tensor), its K/V
     are written, and the device lengths grow by one.  The replay plans its
     work from the device lengths, so every row matches the oracle at the
-    new lengths."""
+    new lengths; a last replay after every length shrank to a few tokens
+    (fewer cost units than the captured grid's waves) too."""
     from paged_kv_attention_06_amd import _lib as L
     w = workloads.make(3, batch=64)
     _announce(f"graph replay with growing lengths: B={w.batch}")
@@ -695,6 +696,17 @@ def test_graph_replay_follows_growing_lengths():
             want.append(po.attention_rows(po.decode(q[s:s + 1], "bf16"), po.decode(Ks[s], "bf16"),
                                           po.decode(Vs[s], "bf16"), [int(lens[s]) - 1], w.scale))
         _check_attention(out, np.concatenate(want), "bf16", f"replay after growth step {step}")
+    # then every length shrinks to 1..5 tokens: fewer cost units than the
+    # captured grid has waves, so the kernel narrows its split of the work
+    lens = rng.integers(1, 6, size=w.batch).astype(np.int32)
+    st.seq_lens.copy_(torch.from_numpy(lens))
+    st.out.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    want = [po.attention_rows(po.decode(q[s:s + 1], "bf16"), po.decode(Ks[s][:lens[s]], "bf16"),
+                              po.decode(Vs[s][:lens[s]], "bf16"), [int(lens[s]) - 1], w.scale)
+            for s in range(w.batch)]
+    _check_attention(st.out.cpu().numpy(), np.concatenate(want), "bf16", "replay after shrinking")
 
 
 @pytest.mark.parametrize("cfg", [5, 4])
@@ -738,3 +750,26 @@ def test_read_probe_checksums(waves):
         for i in ids[a:b]:
             x ^= np.bitwise_xor.reduce(pool[i // w.num_kv_heads, i % w.num_kv_heads].reshape(-1))
         assert got[wv] == x, f"wave {wv} of {waves}"
+
+
+@pytest.mark.parametrize("case", ["long row", "large batch"])
+def test_decode_size_limits(case):
+    """Sizes at the ends of the range the workloads span: one 65,536-token row
+    (4,096 blocks of table, its 8 (row, kv head) items each split over
+    hundreds of waves) beside short ones; and 4,096 sequences of 1..64
+    tokens, whose lengths the kernel scans in 16 chunks of 256.  Every row
+    against the oracle."""
+    rng = np.random.default_rng(131 if case == "long row" else 132)
+    if case == "long row":
+        L = np.array([65536, 1, 17, 300], np.int32)
+    else:
+        L = rng.integers(1, 65, size=4096).astype(np.int32)
+    streams = [np.random.default_rng(x) for x in rng.integers(0, 2**31, 4)]
+    pool = int(1.25 * sum((int(x) + 15) // 16 for x in L)) + 8
+    w = workloads._build(3, f"decode {case}", "bf16", 32, 8, 128, 128 ** -0.5, L - 1,
+                         np.ones(len(L), np.int32), pool, streams)
+    _announce(f"decode {case}: B={w.batch} max L={int(L.max())} pool={pool}")
+    st = gpu_step.run_workload(w)
+    out = st.out.cpu().numpy()
+    want = np.concatenate([scenario.sequence_attention(w, s) for s in range(w.batch)])
+    _check_attention(out, want, "bf16", f"decode {case}")
