@@ -773,3 +773,49 @@ def test_decode_size_limits(case):
     out = st.out.cpu().numpy()
     want = np.concatenate([scenario.sequence_attention(w, s) for s in range(w.batch)])
     _check_attention(out, want, "bf16", f"decode {case}")
+
+
+# ------------------------------------------------------ random shapes (hypothesis)
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as hst  # noqa: E402
+
+
+@hst.composite
+def _random_calls(draw):
+    kind = draw(hst.sampled_from(["decode", "decode", "mixed", "fp8"]))
+    D = draw(hst.sampled_from([64, 128]))
+    hkv = draw(hst.integers(1, 4))
+    B = draw(hst.integers(1, 8))
+    hist = draw(hst.lists(hst.integers(0, 600), min_size=B, max_size=B))
+    if kind == "mixed":
+        G = draw(hst.sampled_from([1, 2, 4]))
+        ql = draw(hst.lists(hst.sampled_from([1, 1, 2, 3, 5, 8, 33, 70, 140]), min_size=B, max_size=B))
+        dtype = "bf16"
+    else:
+        G = draw(hst.sampled_from([1, 2, 4, 8]))
+        ql = [1] * B
+        dtype = draw(hst.sampled_from(["bf16", "bf16", "f32"])) if kind == "decode" else "bf16"
+    seed = draw(hst.integers(0, 2**31 - 1))
+    streams = [np.random.default_rng(seed + k) for k in range(4)]
+    pool = sum((h + q + 15) // 16 for h, q in zip(hist, ql)) + draw(hst.integers(1, 40))
+    return workloads._build(0, f"random {kind}", dtype, hkv * G, hkv, D, D ** -0.5, hist, ql, pool,
+                            streams, cache_dtype="fp8" if kind == "fp8" else "",
+                            kv_scale=workloads.FP8_SCALE if kind == "fp8" else 1.0)
+
+
+@settings(max_examples=32, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(_random_calls())
+def test_random_shapes_against_the_oracle(w):
+    """Random decode, mixed (prefill rows of 2..140 queries beside decode
+    rows, or prefill rows alone) and FP8-cache calls over 1-4 kv heads, 1, 2,
+    4 or 8 query heads per kv head, head sizes 64 and 128, 1-8 sequences of
+    up to 740 tokens in pools with spare blocks: the pool bit for bit and
+    every row within the bars (derandomized, so every run draws the same
+    cases)."""
+    _announce(f"random {w.name}: dtype={w.kv_dtype} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+              f"D={w.head_size} L={w.seq_lens.tolist()} q_len={w.q_len.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"]), "pool differs from the oracle's"
+    _check_attention(st.out.cpu().numpy(), ref["out"], w.dtype, w.name)
