@@ -20,6 +20,10 @@
 
 namespace {
 
+// Default shares of the stream decode's waves (see stream_weights).
+constexpr int kStreamParityWeight = 0;
+constexpr int kStreamAgeWeight = 0;
+
 thread_local std::string g_last_error;
 
 int fail(int code, const char* fmt, ...) {
@@ -181,6 +185,34 @@ int64_t stream_wave_cap(const Plan& p, int hkv) {
   const int64_t t = stream_total(p, hkv);
   const int64_t w = (t + pkv::kStreamMinCost - 1) / pkv::kStreamMinCost;
   return w < pkv::kMaxStreamWaves ? w : pkv::kMaxStreamWaves;
+}
+
+// Shares of the stream decode's waves.  Two effects make waves of equal
+// work end at different times (per-wave timestamps on MI355X, 8B GQA batch
+// of 256, two waves per SIMD): waves of odd workgroup index (which run on
+// the odd XCDs) stream slower, and of the two waves on a SIMD the first
+// dispatched (mostly the first half of the grid) runs ahead.  With
+// PKV_STREAM_WEIGHTS="x,y" (per mille) the even waves take 1 + x and the odd
+// ones 1 - x of an equal share, and the first half of the grid 1 + y, the
+// second half 1 - y; 0,0 gives equal shares.  Used only for calls that fill
+// every SIMD with two waves (W a multiple of 4).
+void stream_weights(int64_t waves, int64_t rounds, bool mixed_call, int* wt, int* half) {
+  for (int k = 0; k < 4; ++k) wt[k] = 1024;
+  *half = (int)waves;
+  int x = kStreamParityWeight, y = kStreamAgeWeight;
+  if (const char* e = std::getenv("PKV_STREAM_WEIGHTS")) {
+    if (std::sscanf(e, "%d,%d", &x, &y) != 2) x = y = 0;
+  }
+  if (mixed_call || rounds != 2 || waves % 4 != 0 || x < 0 || y < 0 || x > 200 || y > 200) return;
+  if (x == 0 && y == 0) return;
+  auto w = [](int sx, int sy, int x, int y) {
+    return (int)std::lround(1024.0 * (1000 + sx * x) * (1000 + sy * y) / 1e6);
+  };
+  wt[0] = w(+1, +1, x, y);
+  wt[1] = w(-1, +1, x, y);
+  wt[2] = w(+1, -1, x, y);
+  wt[3] = 4096 - wt[0] - wt[1] - wt[2];
+  *half = (int)(waves / 2);
 }
 
 // Epochs of stream-decode counters start at a value that differs between
@@ -386,6 +418,8 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
   a.ws_vexp = plan.prefill_vblocks ? reinterpret_cast<int32_t*>(ws + wl.exp_off) : nullptr;
   a.stream_waves = 0;
   a.stream_rounds = 0;
+  for (int k = 0; k < 4; ++k) a.stream_wt[k] = 1024;
+  a.stream_half = 0;
   if (stream_path) {
     static std::atomic<unsigned> epoch{first_epoch()};
     a.stream_waves = (int)waves;
@@ -396,6 +430,7 @@ int attention(const pkv_cache* cache, float* out, const void* q, int32_t num_q_h
     const int simds = 4 * pkv::device_cus();
     const int64_t rounds = simds > 0 ? (waves + simds - 1) / simds : 0;
     a.stream_rounds = (!mixed_call && rounds > 1) ? (int)(rounds < 4 ? rounds : 4) : 0;
+    stream_weights(waves, rounds, mixed_call, a.stream_wt, &a.stream_half);
     // (no decode region when every row is empty: one wave, nothing split)
     const bool region = ws && plan.decode_units > 0;
     a.stream_acc = region ? reinterpret_cast<float*>(ws + pkv::kWorkspaceHeader) : nullptr;

@@ -71,6 +71,8 @@ struct AttnDesc {
   int stream_c0;                   // setup charge per item
   unsigned stream_epoch;           // distinct per call
   int stream_rounds;               // > 1: waves per SIMD, which rotate their issue priority
+  int stream_wt[4];                // shares of the waves (see StreamParams)
+  int stream_half;
   unsigned long long* stream_counters;  // [num_seqs][hkv]
   float* stream_acc;               // [2 * waves][G][D]
   float* stream_ml;                // [2 * waves][G][2]

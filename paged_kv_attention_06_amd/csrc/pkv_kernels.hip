@@ -983,6 +983,12 @@ struct StreamParams {
   int c0;                        // setup charge per item, in steps
   unsigned epoch;                // distinct per call
   int rounds;                    // > 1: waves per SIMD, which rotate their issue priority
+  // Share of the cost line per wave, in units of 1/1024 of an equal share:
+  // waves below `half` weigh wt[0] (even w) or wt[1] (odd w), the others
+  // wt[2] or wt[3].  Equal shares: all 1024 and half = waves.  Otherwise
+  // half = waves / 2, a multiple of 2, and the four sum to 4096.
+  int wt[4];
+  int half;
   unsigned long long* counters;  // [num_seqs][hkv]
   float* part_acc;               // [2 * waves][G][D]
   float* part_ml;                // [2 * waves][G][2]
@@ -997,10 +1003,58 @@ struct StreamCur {
   long long A;  // cost position of step 0 of the item
 };
 
-// Wave whose range holds cost position t: the largest w with
-// floor(w * T / W) <= t.
-__device__ __forceinline__ int stream_wave_of(long long t, long long T, int W) {
-  return (int)(((t + 1) * (long long)W - 1) / T);
+// How the cost line is cut into wave ranges in one call: `waves` ranges,
+// wave w weighing wt[w < half ? 0 : 2] (even w) or wt[... + 1] (odd w), in
+// units of 1/1024 of an equal share.
+struct StreamSplit {
+  int waves, half;
+  int wt[4];
+};
+// Every wave computes the same split from the device total T: the host's
+// weights, unless T is below two units per wave (a call replayed from a
+// graph after the lengths shrank); then max(1, T / 2) waves with equal
+// shares.  Either way every range holds at least one unit (weights stay
+// within half and twice an equal share), so the waves between the first and
+// the last contributor of an item all contribute to it.
+__device__ __forceinline__ StreamSplit stream_split(const StreamParams& sp, long long T) {
+  StreamSplit r;
+  r.waves = sp.waves;
+  r.half = sp.half;
+  for (int k = 0; k < 4; ++k) r.wt[k] = sp.wt[k];
+  if (T < 2LL * sp.waves) {
+    r.waves = (int)max(1LL, T / 2);
+    r.half = r.waves;
+    for (int k = 0; k < 4; ++k) r.wt[k] = 1024;
+  }
+  return r;
+}
+// Weighted position where the range of wave w starts (the sum of the weights
+// of waves 0 .. w - 1; waves * 1024 in all).
+__device__ __forceinline__ long long stream_cum(const StreamSplit& sp, int w) {
+  const int a = min(w, sp.half), b = w - a;
+  return (long long)(a >> 1) * (sp.wt[0] + sp.wt[1]) + (a & 1) * sp.wt[0] +
+         (long long)(b >> 1) * (sp.wt[2] + sp.wt[3]) + (b & 1) * sp.wt[2];
+}
+// First cost position of wave w's range (w = waves gives T).
+__device__ __forceinline__ long long stream_start(const StreamSplit& sp, int w, long long T) {
+  return T * stream_cum(sp, w) / ((long long)sp.waves * 1024);
+}
+// Wave whose range holds cost position t < T: the largest w with
+// stream_start(w) <= t, i.e. the largest w with stream_cum(w) <= u, where u
+// is the largest weighted position with floor(T u / (1024 waves)) <= t.
+__device__ __forceinline__ int stream_wave_of(const StreamSplit& sp, long long t, long long T) {
+  const long long u = ((t + 1) * (long long)sp.waves * 1024 - 1) / T;
+  const long long c_half = stream_cum(sp, sp.half);
+  int w;
+  if (u < c_half) {
+    const long long pr = u / (sp.wt[0] + sp.wt[1]);
+    w = (int)(2 * pr + (u - pr * (sp.wt[0] + sp.wt[1]) >= sp.wt[0] ? 1 : 0));
+  } else {
+    const long long v = u - c_half;
+    const long long pr = v / (sp.wt[2] + sp.wt[3]);
+    w = sp.half + (int)(2 * pr + (v - pr * (sp.wt[2] + sp.wt[3]) >= sp.wt[2] ? 1 : 0));
+  }
+  return min(w, sp.waves - 1);
 }
 
 template <int ES, int D, int G>
@@ -1193,8 +1247,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     for (int off = 32; off > 0; off >>= 1) rest += __shfl_xor(rest, off);
     T += uniform64(rest);
   }
-  const long long cs = (long long)w * T / W;
-  const long long ce = (long long)(w + 1) * T / W;
+  const StreamSplit split = stream_split(sp, T);
+  const long long cs = w < split.waves ? stream_start(split, w, T) : T;
+  const long long ce = w < split.waves ? stream_start(split, w + 1, T) : T;
   if (cs >= ce) {
     zero_rows();
     return;
@@ -1496,8 +1551,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     float l_tot[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) l_tot[g] = wave_sum(l_lane[g]);
-    const int wA = stream_wave_of(c.A, T, W);
-    const int wB = stream_wave_of(c.A + c.n - 1, T, W);
+    const int wA = stream_wave_of(split, c.A, T);
+    const int wB = stream_wave_of(split, c.A + c.n - 1, T);
     float* o = p.out + ((size_t)c.row * hq + (size_t)c.h * G) * D;
     if (wA == wB) {
 #pragma unroll
@@ -1758,6 +1813,8 @@ static hipError_t launch_decode_stream(const CacheDesc& c, const AttnDesc& a, hi
   sp.c0 = a.stream_c0;
   sp.epoch = a.stream_epoch;
   sp.rounds = a.stream_rounds;
+  for (int k = 0; k < 4; ++k) sp.wt[k] = a.stream_wt[k];
+  sp.half = a.stream_half;
   sp.counters = a.stream_counters;
   sp.part_acc = a.stream_acc;
   sp.part_ml = a.stream_ml;
