@@ -546,18 +546,18 @@ __device__ __forceinline__ void pv_block(const uint4 (&vr)[BS * D * ES / 16 / 64
 
 // P.V over one block of an fp8 cache: vr[dd] holds the 16 keys' E4M3 codes
 // of d = 64 dd + lane (one granule per d).  Codes become fp16 pairs (exact)
-// and meet the probabilities, stored in LDS as fp16 [head][32 keys of the
+// and meet the probabilities, stored in LDS as fp16 [head][PS keys of the
 // step], in v_dot2_f32_f16.  Keys at or past `valid_keys` get a zero value,
 // so unwritten slots (any bits, NaN included) cannot reach the sums.
-template <int D, int G, bool CHECK>
+template <int D, int G, bool CHECK, int PS = 32>
 __device__ __forceinline__ void pv_block_fp8(const uint4 (&vr)[D / 64], const uint16_t* __restrict__ p16,
                                              int key_base, int valid_keys, float (&acc)[G][D / 64]) {
   constexpr int DPL = D / 64;
   uint32_t pp[G][8];  // probability pairs (keys 2q, 2q + 1) of each head
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p16 + g * 32 + key_base);
-    const uint4 b = *reinterpret_cast<const uint4*>(p16 + g * 32 + key_base + 8);
+    const uint4 a = *reinterpret_cast<const uint4*>(p16 + g * PS + key_base);
+    const uint4 b = *reinterpret_cast<const uint4*>(p16 + g * PS + key_base + 8);
     pp[g][0] = a.x; pp[g][1] = a.y; pp[g][2] = a.z; pp[g][3] = a.w;
     pp[g][4] = b.x; pp[g][5] = b.y; pp[g][6] = b.z; pp[g][7] = b.w;
   }
@@ -597,6 +597,27 @@ template <int ES, int D>
 struct StepRegs {
   uint4 k[DecodeShape<ES, D>::KH];
   uint4 v[2][DecodeShape<ES, D>::VG];
+};
+
+// Steps of the stream decode.  A wave's rate grows with the bytes of one
+// step more than with the number of waves holding steps in flight: on the
+// 8B GQA batch, one bf16 wave per SIMD (16 KiB steps) streamed 4.93 TB/s
+// where two FP8 waves per SIMD with 8 KiB steps reached 4.00 and three 4.48.
+// So an FP8 step covers four blocks (16 KiB of K and V at D = 128) and each
+// lane takes one token's whole K row; the other caches keep two blocks per
+// step, each lane half a K row.
+template <int ES, int D>
+struct StreamShape {
+  static constexpr int NB = ES == 1 ? 4 : 2;                     // blocks per step
+  static constexpr int STEP = NB * BS;                           // tokens per step
+  static constexpr int KL = ES == 1 ? DecodeShape<ES, D>::KG     // K granules per lane
+                                    : DecodeShape<ES, D>::KH;
+  static_assert(ES != 1 || STEP == 64, "one token per lane");
+};
+template <int ES, int D>
+struct StreamRegs {
+  uint4 k[StreamShape<ES, D>::KL];
+  uint4 v[StreamShape<ES, D>::NB][DecodeShape<ES, D>::VG];
 };
 
 // Per-item state of a decode wave: which unit of which row, and where.
@@ -832,10 +853,13 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int item, cha
 
 // Waves per SIMD the decode kernels are compiled for: two, except where
 // their registers do not fit in half the register file (fp32 at D = 128 or
-// G = 8; bf16 at D = 128 and G = 8): those get one wave per SIMD and all 512
-// registers, so nothing spills to memory.
+// G = 8; bf16 at D = 128 and G = 8; FP8 at G = 8): those get one wave per
+// SIMD and all 512 registers, so nothing spills to memory.
 constexpr int decode_waves_per_simd(int es, int d, int g) {
-  return (es == 4 && (d == 128 || g == 8)) || (es == 2 && d == 128 && g == 8) ? 1 : 2;
+  return (es == 4 && (d == 128 || g == 8)) || (es == 2 && d == 128 && g == 8) ||
+                 (es == 1 && g == 8)
+             ? 1
+             : 2;
 }
 
 template <int ES, int D, int G>
@@ -1166,11 +1190,14 @@ template <int ES, int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     decode_waves_per_simd(ES, D, G)))) void k_decode_stream(StreamParams sp) {
   using S = DecodeShape<ES, D>;
+  using SS = StreamShape<ES, D>;
   constexpr int QBUF = StreamLds<ES, D, G>::QBUF;
   constexpr int QGR = G * S::QKG;            // 16-byte granules of one item's q rows
   constexpr int NQ = (QGR + 63) / 64;        // per lane
   __shared__ __align__(16) char q_lds[QBUF];
+  // one step's probabilities: fp32 [32 keys][G], or (FP8) fp16 [G][64 keys]
   __shared__ __align__(16) float p_lds[32 * G];
+  static_assert(SS::STEP * (ES == 1 ? 2 : 4) == 128, "a step's probabilities fill p_lds");
   __shared__ int len_lds[256];
   __shared__ int row_lds[256];
 
@@ -1210,7 +1237,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // have changed still covers every item (the grid and the workspace depend
   // on the wave count and the number of sequences, not on the lengths).
   auto cost_of = [&](int L) -> long long {
-    return L > 0 ? (long long)hkv * ((L + 31) / 32 + c0) : 0;
+    return L > 0 ? (long long)hkv * ((L + SS::STEP - 1) / SS::STEP + c0) : 0;
   };
   struct ChunkCost {
     long long c[4], tot, incl;  // this lane's costs, their sum, inclusive scan over lanes
@@ -1321,7 +1348,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   StreamCur cur0;
   {
     const int L = len_of(s_found);
-    const int n = (L + 31) / 32;
+    const int n = (L + SS::STEP - 1) / SS::STEP;
     const long long h = (cs - S_found) / (n + c0);
     cur0.s = s_found;
     cur0.h = (int)h;
@@ -1365,15 +1392,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     r.s = s;
     r.h = 0;
     r.L = L;
-    r.n = (L + 31) / 32;
+    r.n = (L + SS::STEP - 1) / SS::STEP;
     r.row = row_of(s);
     return r;
   };
 
-  // block ids of a step: lane l gets block 2j + (l & 1) of the item's row
+  // block ids of a step: lane l gets block NB j + k of the item's row, k =
+  // l / 16 (FP8: the block of the lane's token) or l % NB; lane id_lane(k)
+  // holds block k.
+  auto id_lane = [](int k) { return ES == 1 ? 16 * k : k; };
   auto load_ids = [&](const StreamCur& c) -> int {
     const int nblk = (c.L + BS - 1) / BS;
-    const int b = min(2 * c.j + (lane & 1), nblk - 1);
+    const int b = min(SS::NB * c.j + (ES == 1 ? lane >> 4 : lane % SS::NB), nblk - 1);
     return p.block_tables[(size_t)c.s * p.max_blocks + b];
   };
   auto load_q = [&](uint4 (&qr)[NQ], const StreamCur& c) {
@@ -1401,18 +1431,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   const int t_in_blk = (lane >> 1) & 15;
   const int bsel = lane >> 5;
   const int k_lane_off = (half * S::KH * BS + t_in_blk) * 16;
-  auto load_kv = [&](StepRegs<ES, D>& r, int h, int b0, int b1) {
+  // K/V of a step whose blocks are lb[0 .. NB) (lid: the lane's value of
+  // the same ids): the lane's K granules (FP8: token lane of the step, in
+  // block lane / 16, the whole row; otherwise token t_in_blk of block bsel,
+  // half row `half`), then the V tiles, one granule per d and block.
+  auto load_kv = [&](StreamRegs<ES, D>& r, int h, const int (&lb)[SS::NB], int lid) {
     const char* head_base = p.kv + (size_t)h * 2 * S::TILE;
-    const char* base0 = head_base + (size_t)b0 * p.block_bytes;
-    const char* base1 = head_base + (size_t)b1 * p.block_bytes;
-    const char* kp = (bsel ? base1 : base0) + k_lane_off;
-#pragma unroll
-    for (int cc = 0; cc < S::KH; ++cc) r.k[cc] = load_once(kp + cc * BS * 16);
-#pragma unroll
-    for (int i = 0; i < S::VG; ++i) {
-      r.v[0][i] = load_once(base0 + S::TILE + i * 1024 + lane * 16);
-      r.v[1][i] = load_once(base1 + S::TILE + i * 1024 + lane * 16);
+    const char* kp;
+    if constexpr (ES == 1) {
+      kp = head_base + (size_t)lid * p.block_bytes + (lane & 15) * 16;
+    } else {
+      kp = head_base + (size_t)(bsel ? lb[1] : lb[0]) * p.block_bytes + k_lane_off;
     }
+#pragma unroll
+    for (int cc = 0; cc < SS::KL; ++cc) r.k[cc] = load_once(kp + cc * BS * 16);
+#pragma unroll
+    for (int i = 0; i < S::VG; ++i)
+#pragma unroll
+      for (int jb = 0; jb < SS::NB; ++jb)
+        r.v[jb][i] = load_once(head_base + (size_t)lb[jb] * p.block_bytes + S::TILE + i * 1024 +
+                               lane * 16);
   };
 
   float m_run[G], l_lane[G], acc[G][S::DPL];
@@ -1426,16 +1464,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  auto compute = [&](const StepRegs<ES, D>& r, const StreamCur& c) {
+  auto compute = [&](const StreamRegs<ES, D>& r, const StreamCur& c) {
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
     const char* qh = q_lds + half * S::QROW;
     if constexpr (ES == 1) {
-      // K granule cc holds 16 E4M3 codes (d = 16 cc .. of this half row),
-      // converted pairwise to bf16 (exact) for v_dot2 against two q granules
+      // The lane's token against every head: K granule cc holds the 16 E4M3
+      // codes of d = 16 cc .., converted pairwise to bf16 (exact) for v_dot2
+      // against q granules 2 cc and 2 cc + 1 (one half row holds both).
 #pragma unroll
-      for (int cc = 0; cc < S::KH; ++cc) {
+      for (int cc = 0; cc < SS::KL; ++cc) {
         const uint4 kg = r.k[cc];
         const uint32_t kw[4] = {kg.x, kg.y, kg.z, kg.w};
         uint32_t kb[8];
@@ -1446,8 +1485,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const uint4 q0 = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + (2 * cc) * 16);
-          const uint4 q1 = *reinterpret_cast<const uint4*>(qh + g * 2 * S::QROW + (2 * cc + 1) * 16);
+          const char* qp = q_lds + (g * 2 + 2 * cc / S::QKH) * S::QROW + (2 * cc % S::QKH) * 16;
+          const uint4 q0 = *reinterpret_cast<const uint4*>(qp);
+          const uint4 q1 = *reinterpret_cast<const uint4*>(qp + 16);
           const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -1493,11 +1533,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
       for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
     }
     }
-    const int tok0 = c.j * 32;
-    const bool tok_ok = tok0 + (lane >> 1) < c.L;
+    const int tok0 = c.j * SS::STEP;
+    const bool tok_ok = tok0 + (ES == 1 ? lane : lane >> 1) < c.L;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float full = sc[g] + dpp_f<0xB1>(sc[g]);
+      const float full = ES == 1 ? sc[g] : sc[g] + dpp_f<0xB1>(sc[g]);
       const float x = tok_ok ? full * p.scale_log2 : -INFINITY;
       const float mi = wave_max(x);
       if (mi > m_run[g] + kRescaleSlack) {
@@ -1508,27 +1548,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
         m_run[g] = mi;
       }
       const float pr = __builtin_amdgcn_exp2f(x - m_run[g]);
-      if (half == 0) {
-        if constexpr (ES == 1) {  // fp16 probabilities; the sums use the same rounded values
-          const _Float16 ph = (_Float16)pr;
-          l_lane[g] += (float)ph;
-          reinterpret_cast<_Float16*>(p_lds)[g * 32 + (lane >> 1)] = ph;
-        } else {
-          l_lane[g] += pr;
-          p_lds[(lane >> 1) * G + g] = pr;
-        }
+      if constexpr (ES == 1) {  // fp16 probabilities; the sums use the same rounded values
+        const _Float16 ph = (_Float16)pr;
+        l_lane[g] += (float)ph;
+        reinterpret_cast<_Float16*>(p_lds)[g * SS::STEP + lane] = ph;
+      } else if (half == 0) {
+        l_lane[g] += pr;
+        p_lds[(lane >> 1) * G + g] = pr;
       }
     }
     wave_sync();
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+    for (int jb = 0; jb < SS::NB; ++jb) {
       const int valid = c.L - (tok0 + jb * BS);
       if constexpr (ES == 1) {
         const uint16_t* p16 = reinterpret_cast<const uint16_t*>(p_lds);
         if (valid >= BS)
-          pv_block_fp8<D, G, false>(r.v[jb], p16, jb * BS, BS, acc);
+          pv_block_fp8<D, G, false, SS::STEP>(r.v[jb], p16, jb * BS, BS, acc);
         else if (valid > 0)
-          pv_block_fp8<D, G, true>(r.v[jb], p16, jb * BS, valid, acc);
+          pv_block_fp8<D, G, true, SS::STEP>(r.v[jb], p16, jb * BS, valid, acc);
       } else {
         if (valid >= BS)
           pv_block<ES, D, G, false>(r.v[jb], p_lds, jb * BS, BS, acc);
@@ -1591,22 +1629,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // after), so the compiler's wait counts stay exact on all paths: past the
   // end of the range the ids come from the current step and the K/V are a
   // re-read of the current step's blocks (an L2 hit).
-  StepRegs<ES, D> ra, rb;
+  StreamRegs<ES, D> ra, rb;
   uint4 qa[NQ], qb[NQ];
   load_q(qa, cur0);
   int ids_a = load_ids(cur0);  // ids of the step whose K/V go to ra
   StreamCur cur1 = next(cur0);
   int ids_b = load_ids(cur1.valid ? cur1 : cur0);
-  int lb0 = uniform(__builtin_amdgcn_readlane(ids_a, 0));  // blocks of the last K/V issued
-  int lb1 = uniform(__builtin_amdgcn_readlane(ids_a, 1));
-  load_kv(ra, cur0.h, lb0, lb1);
+  int lb[SS::NB];  // blocks of the last K/V issued
+  int lid = 0;     // the same, as load_ids gave them to this lane
+  auto take_ids = [&](int ids) {
+#pragma unroll
+    for (int k = 0; k < SS::NB; ++k) lb[k] = uniform(__builtin_amdgcn_readlane(ids, id_lane(k)));
+    lid = ids;
+  };
+  take_ids(ids_a);
+  load_kv(ra, cur0.h, lb, lid);
   bool new0 = true;
   reset_state();
 
   // One step: compute `c` (data in rc, q rows in qc if it starts an item),
   // with `cn` = the step after (K/V -> rn, q -> qn) and the step after that
   // (its ids -> ids_out).
-  auto half_step = [&](StepRegs<ES, D>& rc, StepRegs<ES, D>& rn, uint4 (&qc)[NQ], uint4 (&qn)[NQ],
+  auto half_step = [&](StreamRegs<ES, D>& rc, StreamRegs<ES, D>& rn, uint4 (&qc)[NQ], uint4 (&qn)[NQ],
                        const StreamCur& c, StreamCur& cn, int ids_n, int& ids_out, bool& new_c) {
     StreamCur c2 = next(cn);
     const bool new_n = cn.valid && (cn.s != c.s || cn.h != c.h);
@@ -1614,11 +1658,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     ids_out = load_ids(c2.valid ? c2 : c);
     int hh = c.h;
     if (cn.valid) {
-      lb0 = uniform(__builtin_amdgcn_readlane(ids_n, 0));
-      lb1 = uniform(__builtin_amdgcn_readlane(ids_n, 1));
+      take_ids(ids_n);
       hh = cn.h;
     }
-    load_kv(rn, hh, lb0, lb1);
+    load_kv(rn, hh, lb, lid);
     if (new_c) {
       store_q(qc);
       wave_sync();
@@ -1800,9 +1843,9 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
   //  - bf16: two waves per SIMD, 0.267 ms against 0.284 ms with one, whose
   //    single chain of requests hides those misses less well (back to back,
   //    with the blocks still cached, one wave is the faster: 0.260 vs 0.267);
-  //  - fp8 (half the bytes per step, more arithmetic): three waves per SIMD,
-  //    0.164 ms against 0.175 with two (back to back: 0.161 vs 0.151).
-  const int per_cu = dtype_bytes == 1 ? 12 : 8;
+  //  - fp8: two waves per SIMD of four-block steps (two-block steps, the
+  //    earlier design, wanted three waves and still streamed slower).
+  const int per_cu = 8;
   return (nb < per_cu ? nb : per_cu) * cus;
 }
 
