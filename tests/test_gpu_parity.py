@@ -627,6 +627,27 @@ def test_decode_wide_groups_and_fp32_head128(kv, G, D):
     _check_attention(st.out.cpu().numpy(), ref["out"], dtype, f"decode {kv} G={G} D={D}")
 
 
+@pytest.mark.parametrize("G,D", [(4, 128), (1, 128), (2, 64), (4, 64)])
+def test_fp8_decode_step_edges(G, D):
+    """FP8 caches decode in steps of four blocks (64 tokens): lengths at and
+    around every block and step edge of the first 257 tokens, and one
+    4097-token row that the stream split shares among many waves; the pool
+    bit for bit and every row against the oracle."""
+    L = np.array([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 127, 128, 129, 191, 192,
+                  193, 255, 256, 257, 4097], np.int32)
+    hkv = 4
+    streams = [np.random.default_rng(x) for x in (201 + G, 202 + D, 203, 204)]
+    pool = int(1.25 * sum((int(x) + 15) // 16 for x in L)) + 8
+    w = workloads._build(3, f"fp8 step edges G={G} D={D}", "bf16", hkv * G, hkv, D, D ** -0.5,
+                         L - 1, np.ones(len(L), np.int32), pool, streams, cache_dtype="fp8",
+                         kv_scale=workloads.FP8_SCALE)
+    _announce(f"fp8 step edges G={G} D={D}: L={L.tolist()}")
+    st = gpu_step.run_workload(w)
+    ref = scenario.run_step(w)
+    assert np.array_equal(st.pool_codes(), ref["pool"]), "fp8 pool differs from the oracle's"
+    _check_attention(st.out.cpu().numpy(), ref["out"], "bf16", f"fp8 step edges G={G} D={D}")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8"])
 def test_decode_batch_of_empty_rows_is_zero(kv):
     """A decode call whose every sequence has length 0 returns PKV_OK and
