@@ -665,17 +665,29 @@ def test_decode_batch_of_empty_rows_is_zero(kv):
     assert torch.count_nonzero(st.out).item() == 0
 
 
-def test_graph_replay_follows_growing_lengths():
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_graph_replay_follows_growing_lengths(kv):
     """A decode call captured once and replayed for three more decode steps:
     before each replay every sequence appends one token through the
     library's allocator (new blocks enter the same table tensor), its K/V
-    are written, and the device lengths grow by one.  The replay plans its
-    work from the device lengths, so every row matches the oracle at the
-    new lengths; a last replay after every length shrank to a few tokens
-    (fewer cost units than the captured grid's waves) too."""
+    are written (an FP8 cache quantizes them), and the device lengths grow
+    by one.  The replay plans its work from the device lengths, so every row
+    matches the oracle at the new lengths; a last replay after every length
+    shrank to a few tokens (fewer cost units than the captured grid's waves)
+    too."""
     from paged_kv_attention_06_amd import _lib as L
     w = workloads.make(3, batch=64)
-    _announce(f"graph replay with growing lengths: B={w.batch}")
+    if kv == "fp8":  # as workloads.make_fp8 does for the full-size batch
+        w.cache_dtype = "fp8"
+        w.k_scale = w.v_scale = workloads.FP8_SCALE
+        w.pool_fill = workloads.FP8_NAN
+
+    def values(codes, scale):  # what the cache holds, as float64
+        if kv == "fp8":
+            return po.decode(po.fp8_quantize(codes, scale), "fp8") * scale
+        return po.decode(codes, "bf16")
+
+    _announce(f"graph replay with growing lengths: B={w.batch}, {kv} cache")
     st = gpu_step.PagedStep(w)
     st.max_blocks += 1
     st.tables = np.zeros((w.batch, st.max_blocks), np.int32)
@@ -714,9 +726,9 @@ def test_graph_replay_follows_growing_lengths():
         for s in range(w.batch):
             Ks[s] = np.concatenate([Ks[s], k_new[s:s + 1]])
             Vs[s] = np.concatenate([Vs[s], v_new[s:s + 1]])
-            want.append(po.attention_rows(po.decode(q[s:s + 1], "bf16"), po.decode(Ks[s], "bf16"),
-                                          po.decode(Vs[s], "bf16"), [int(lens[s]) - 1], w.scale))
-        _check_attention(out, np.concatenate(want), "bf16", f"replay after growth step {step}")
+            want.append(po.attention_rows(po.decode(q[s:s + 1], "bf16"), values(Ks[s], w.k_scale),
+                                          values(Vs[s], w.v_scale), [int(lens[s]) - 1], w.scale))
+        _check_attention(out, np.concatenate(want), "bf16", f"{kv} replay after growth step {step}")
     # then every length shrinks to 1..5 tokens: fewer cost units than the
     # captured grid has waves, so the kernel narrows its split of the work
     lens = rng.integers(1, 6, size=w.batch).astype(np.int32)
@@ -724,10 +736,11 @@ def test_graph_replay_follows_growing_lengths():
     st.out.fill_(float("nan"))
     g.replay()
     torch.cuda.synchronize()
-    want = [po.attention_rows(po.decode(q[s:s + 1], "bf16"), po.decode(Ks[s][:lens[s]], "bf16"),
-                              po.decode(Vs[s][:lens[s]], "bf16"), [int(lens[s]) - 1], w.scale)
+    want = [po.attention_rows(po.decode(q[s:s + 1], "bf16"), values(Ks[s][:lens[s]], w.k_scale),
+                              values(Vs[s][:lens[s]], w.v_scale), [int(lens[s]) - 1], w.scale)
             for s in range(w.batch)]
-    _check_attention(st.out.cpu().numpy(), np.concatenate(want), "bf16", "replay after shrinking")
+    _check_attention(st.out.cpu().numpy(), np.concatenate(want), "bf16",
+                     f"{kv} replay after shrinking")
 
 
 @pytest.mark.parametrize("cfg", [5, 4])
