@@ -2,8 +2,8 @@
 against paged_attention_decode with a caller workspace, through the C ABI:
 two calls in a row on the library's scratch array, the second with a
 smaller batch, each equal bit for bit to the workspace call and within the
-bars of the oracle; and a batch too large for the array is refused before
-any launch."""
+bars of the oracle (bf16 and FP8 caches); and a batch too large for the
+array is refused before any launch."""
 import sys
 
 import numpy as np
@@ -40,11 +40,23 @@ def _against_oracle(out, w, what):
     assert max_abs <= 5e-3 and rel <= 1e-3, f"{what}: max|d| {max_abs:.3e} rel {rel:.3e}"
 
 
-def test_noalloc_decode_equals_workspace_decode_twice():
+def _fp8(w):
+    """The same batch with an FP8 E4M3 cache (as workloads.make_fp8 builds it)."""
+    w.name = w.name + " (fp8 KV)"
+    w.cache_dtype = "fp8"
+    w.k_scale = w.v_scale = workloads.FP8_SCALE
+    w.pool_fill = workloads.FP8_NAN
+    return w
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_noalloc_decode_equals_workspace_decode_twice(kv):
     first = workloads.make(3)                  # the 8B GQA batch of 256
     second = workloads.make(3, batch=40)       # a smaller batch on the same scratch
+    if kv == "fp8":
+        first, second = _fp8(first), _fp8(second)
     for w in (first, second):
-        _announce(f"no-allocation decode: B={w.batch} sum L={int(w.seq_lens.sum())}")
+        _announce(f"no-allocation decode ({kv} cache): B={w.batch} sum L={int(w.seq_lens.sum())}")
         st = gpu_step.run_workload(w)          # workspace call: st.out
         out = torch.full_like(st.out, float("nan"))
         _noalloc(st, w, out)
