@@ -962,7 +962,8 @@ __global__ __launch_bounds__(256) void k_decode_merge(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Stream decode (calls without prefill rows).  The decode work is laid out
 // on one line of cost: item (row s, kv head h), h fastest, costs a setup
-// charge c0 followed by one unit per 32-token step of the row.  The line is
+// charge c0 followed by one unit per step of the row (32 tokens; 64 for an
+// FP8 cache, see StreamShape).  The line is
 // cut into `waves` equal ranges, one per wave, and the grid is sized to the
 // waves the GPU holds at once, so every wave streams the same number of
 // steps and all finish together: there is no tail of short units.
