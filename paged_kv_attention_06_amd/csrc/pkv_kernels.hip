@@ -604,20 +604,25 @@ struct StepRegs {
 // 8B GQA batch, one bf16 wave per SIMD (16 KiB steps) streamed 4.93 TB/s
 // where two FP8 waves per SIMD with 8 KiB steps reached 4.00 and three 4.48.
 // So an FP8 step covers four blocks (16 KiB of K and V at D = 128) and each
-// lane takes one token's whole K row; the other caches keep two blocks per
-// step, each lane half a K row.
-template <int ES, int D>
+// lane takes one token's whole K row.  bf16 with one query head per kv head
+// takes four-block steps too (32 KiB at D = 128, one wave per SIMD: 13B
+// shape 0.805-0.810 of 8 TB/s against 0.795-0.798, 7B 0.713-0.714 against
+// 0.710-0.712); with more heads per kv head one wave cannot overlap their
+// arithmetic with its loads (8B GQA: 0.64 against 0.68), so those and fp32
+// keep two blocks per step, each lane half a K row.
+template <int ES, int D, int G>
 struct StreamShape {
-  static constexpr int NB = ES == 1 ? 4 : 2;                     // blocks per step
+  static constexpr int NB = ES == 1 || (ES == 2 && G == 1) ? 4 : 2;  // blocks per step
   static constexpr int STEP = NB * BS;                           // tokens per step
-  static constexpr int KL = ES == 1 ? DecodeShape<ES, D>::KG     // K granules per lane
-                                    : DecodeShape<ES, D>::KH;
-  static_assert(ES != 1 || STEP == 64, "one token per lane");
+  static constexpr bool TPL = NB == 4;                           // one token per lane
+  static constexpr int KL = TPL ? DecodeShape<ES, D>::KG         // K granules per lane
+                                : DecodeShape<ES, D>::KH;
+  static_assert(!TPL || STEP == 64, "one token per lane");
 };
-template <int ES, int D>
+template <int ES, int D, int G>
 struct StreamRegs {
-  uint4 k[StreamShape<ES, D>::KL];
-  uint4 v[StreamShape<ES, D>::NB][DecodeShape<ES, D>::VG];
+  uint4 k[StreamShape<ES, D, G>::KL];
+  uint4 v[StreamShape<ES, D, G>::NB][DecodeShape<ES, D>::VG];
 };
 
 // Per-item state of a decode wave: which unit of which row, and where.
@@ -853,10 +858,11 @@ __device__ __forceinline__ void decode_item(const DecodeParams& p, int item, cha
 
 // Waves per SIMD the decode kernels are compiled for: two, except where
 // their registers do not fit in half the register file (fp32 at D = 128 or
-// G = 8; bf16 at D = 128 and G = 8; FP8 at G = 8): those get one wave per
-// SIMD and all 512 registers, so nothing spills to memory.
+// G = 8; bf16 at D = 128 and G = 8, or G = 1 with its four-block steps; FP8
+// at G = 8): those get one wave per SIMD and all 512 registers, so nothing
+// spills to memory.
 constexpr int decode_waves_per_simd(int es, int d, int g) {
-  return (es == 4 && (d == 128 || g == 8)) || (es == 2 && d == 128 && g == 8) ||
+  return (es == 4 && (d == 128 || g == 8)) || (es == 2 && d == 128 && (g == 8 || g == 1)) ||
                  (es == 1 && g == 8)
              ? 1
              : 2;
@@ -962,8 +968,8 @@ __global__ __launch_bounds__(256) void k_decode_merge(DecodeParams p) {
 // ---------------------------------------------------------------------------
 // Stream decode (calls without prefill rows).  The decode work is laid out
 // on one line of cost: item (row s, kv head h), h fastest, costs a setup
-// charge c0 followed by one unit per step of the row (32 tokens; 64 for an
-// FP8 cache, see StreamShape).  The line is
+// charge c0 followed by one unit per step of the row (32 or 64 tokens, see
+// StreamShape).  The line is
 // cut into `waves` equal ranges, one per wave, and the grid is sized to the
 // waves the GPU holds at once, so every wave streams the same number of
 // steps and all finish together: there is no tail of short units.
@@ -1191,14 +1197,14 @@ template <int ES, int D, int G>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     decode_waves_per_simd(ES, D, G)))) void k_decode_stream(StreamParams sp) {
   using S = DecodeShape<ES, D>;
-  using SS = StreamShape<ES, D>;
+  using SS = StreamShape<ES, D, G>;
   constexpr int QBUF = StreamLds<ES, D, G>::QBUF;
   constexpr int QGR = G * S::QKG;            // 16-byte granules of one item's q rows
   constexpr int NQ = (QGR + 63) / 64;        // per lane
   __shared__ __align__(16) char q_lds[QBUF];
-  // one step's probabilities: fp32 [32 keys][G], or (FP8) fp16 [G][64 keys]
-  __shared__ __align__(16) float p_lds[32 * G];
-  static_assert(SS::STEP * (ES == 1 ? 2 : 4) == 128, "a step's probabilities fill p_lds");
+  // one step's probabilities: fp32 [keys of the step][G], or (FP8) fp16
+  // [G][64 keys]
+  __shared__ __align__(16) float p_lds[SS::STEP * (ES == 1 ? 2 : 4) / 4 * G];
   __shared__ int len_lds[256];
   __shared__ int row_lds[256];
 
@@ -1401,10 +1407,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // block ids of a step: lane l gets block NB j + k of the item's row, k =
   // l / 16 (FP8: the block of the lane's token) or l % NB; lane id_lane(k)
   // holds block k.
-  auto id_lane = [](int k) { return ES == 1 ? 16 * k : k; };
+  auto id_lane = [](int k) { return SS::TPL ? 16 * k : k; };
   auto load_ids = [&](const StreamCur& c) -> int {
     const int nblk = (c.L + BS - 1) / BS;
-    const int b = min(SS::NB * c.j + (ES == 1 ? lane >> 4 : lane % SS::NB), nblk - 1);
+    const int b = min(SS::NB * c.j + (SS::TPL ? lane >> 4 : lane % SS::NB), nblk - 1);
     return p.block_tables[(size_t)c.s * p.max_blocks + b];
   };
   auto load_q = [&](uint4 (&qr)[NQ], const StreamCur& c) {
@@ -1433,13 +1439,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   const int bsel = lane >> 5;
   const int k_lane_off = (half * S::KH * BS + t_in_blk) * 16;
   // K/V of a step whose blocks are lb[0 .. NB) (lid: the lane's value of
-  // the same ids): the lane's K granules (FP8: token lane of the step, in
-  // block lane / 16, the whole row; otherwise token t_in_blk of block bsel,
-  // half row `half`), then the V tiles, one granule per d and block.
-  auto load_kv = [&](StreamRegs<ES, D>& r, int h, const int (&lb)[SS::NB], int lid) {
+  // the same ids): the lane's K granules (four-block steps: token lane of
+  // the step, in block lane / 16, the whole row; otherwise token t_in_blk of
+  // block bsel, half row `half`), then the V tiles, one granule per d and
+  // block.
+  auto load_kv = [&](StreamRegs<ES, D, G>& r, int h, const int (&lb)[SS::NB], int lid) {
     const char* head_base = p.kv + (size_t)h * 2 * S::TILE;
     const char* kp;
-    if constexpr (ES == 1) {
+    if constexpr (SS::TPL) {
       kp = head_base + (size_t)lid * p.block_bytes + (lane & 15) * 16;
     } else {
       kp = head_base + (size_t)(bsel ? lb[1] : lb[0]) * p.block_bytes + k_lane_off;
@@ -1465,7 +1472,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  auto compute = [&](const StreamRegs<ES, D>& r, const StreamCur& c) {
+  auto compute = [&](const StreamRegs<ES, D, G>& r, const StreamCur& c) {
     float sc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) sc[g] = 0.f;
@@ -1494,6 +1501,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
           for (int e = 0; e < 8; ++e)
             sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[e]),
                                                     __builtin_bit_cast(bf16x2_t, kb[e]), sc[g], false);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
+      }
+    } else if constexpr (SS::TPL) {
+      // bf16, the lane's token against every head: K granule cc and q
+      // granule cc hold the same 8 d values
+#pragma unroll
+      for (int cc = 0; cc < SS::KL; ++cc) {
+        const uint4 kg = r.k[cc];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint4 qg = *reinterpret_cast<const uint4*>(
+              q_lds + (g * 2 + cc / S::QKH) * S::QROW + (cc % S::QKH) * 16);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.x),
+                                                  __builtin_bit_cast(bf16x2_t, kg.x), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.y),
+                                                  __builtin_bit_cast(bf16x2_t, kg.y), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.z),
+                                                  __builtin_bit_cast(bf16x2_t, kg.z), sc[g], false);
+          sc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qg.w),
+                                                  __builtin_bit_cast(bf16x2_t, kg.w), sc[g], false);
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) asm volatile("" : "+v"(sc[g]));
@@ -1535,10 +1564,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
     }
     }
     const int tok0 = c.j * SS::STEP;
-    const bool tok_ok = tok0 + (ES == 1 ? lane : lane >> 1) < c.L;
+    const bool tok_ok = tok0 + (SS::TPL ? lane : lane >> 1) < c.L;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float full = ES == 1 ? sc[g] : sc[g] + dpp_f<0xB1>(sc[g]);
+      const float full = SS::TPL ? sc[g] : sc[g] + dpp_f<0xB1>(sc[g]);
       const float x = tok_ok ? full * p.scale_log2 : -INFINITY;
       const float mi = wave_max(x);
       if (mi > m_run[g] + kRescaleSlack) {
@@ -1553,6 +1582,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
         const _Float16 ph = (_Float16)pr;
         l_lane[g] += (float)ph;
         reinterpret_cast<_Float16*>(p_lds)[g * SS::STEP + lane] = ph;
+      } else if (SS::TPL) {
+        l_lane[g] += pr;
+        p_lds[lane * G + g] = pr;
       } else if (half == 0) {
         l_lane[g] += pr;
         p_lds[(lane >> 1) * G + g] = pr;
@@ -1633,7 +1665,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // loaded two steps ahead have arrived when their K/V are issued; loaded
   // one step ahead, the issue could wait on a load only one step old (8B
   // GQA batch: 0.674-0.676 of 8 TB/s against 0.669-0.671).
-  StreamRegs<ES, D> ra, rb;
+  StreamRegs<ES, D, G> ra, rb;
   uint4 qa[NQ], qb[NQ];
   load_q(qa, cur0);
   int ids_a = load_ids(cur0);  // ids of the step whose K/V go to ra
@@ -1657,7 +1689,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   // with `cn` = the step after (K/V -> rn, q -> qn; its ids in ids_n) and
   // `cf` the one after that (ids in ids_f); loads the ids of the step after
   // `cf`, which it returns, and shifts ids_f into ids_n.
-  auto half_step = [&](StreamRegs<ES, D>& rc, StreamRegs<ES, D>& rn, uint4 (&qc)[NQ], uint4 (&qn)[NQ],
+  auto half_step = [&](StreamRegs<ES, D, G>& rc, StreamRegs<ES, D, G>& rn, uint4 (&qc)[NQ], uint4 (&qn)[NQ],
                        const StreamCur& c, StreamCur& cn, const StreamCur& cf, int& ids_n, int& ids_f,
                        bool& new_c) {
     StreamCur c2 = next(cf);
