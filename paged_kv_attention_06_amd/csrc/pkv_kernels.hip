@@ -1405,8 +1405,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(
   };
 
   // block ids of a step: lane l gets block NB j + k of the item's row, k =
-  // l / 16 (FP8: the block of the lane's token) or l % NB; lane id_lane(k)
-  // holds block k.
+  // l / 16 (four-block steps: the block of the lane's token) or l % NB;
+  // lane id_lane(k) holds block k.
   auto id_lane = [](int k) { return SS::TPL ? 16 * k : k; };
   auto load_ids = [&](const StreamCur& c) -> int {
     const int nblk = (c.L + BS - 1) / BS;
@@ -1887,7 +1887,9 @@ int decode_stream_slots(int dtype_bytes, int D, int G) {
   //    single chain of requests hides those misses less well (back to back,
   //    with the blocks still cached, one wave is the faster: 0.260 vs 0.267);
   //  - fp8: two waves per SIMD of four-block steps (two-block steps, the
-  //    earlier design, wanted three waves and still streamed slower).
+  //    earlier design, wanted three waves and still streamed slower);
+  //  - bf16 with one query head per kv head at D = 128: one wave per SIMD
+  //    of four-block steps (its registers need the whole file).
   const int per_cu = 8;
   return (nb < per_cu ? nb : per_cu) * cus;
 }
