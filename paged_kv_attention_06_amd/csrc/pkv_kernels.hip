@@ -2387,10 +2387,14 @@ __device__ __forceinline__ void prefill_item(const PrefillParams& p, int work, c
       lo[w] = __builtin_bit_cast(
           uint32_t, __builtin_convertvector((f32x2_t){a - bf16_lo(hw), b - bf16_hi(hw)}, bf16x2_t));
     } else {
-      // P in fp16; l sums the same rounded values that enter the product
-      const f16x2_t one = {(_Float16)1.f, (_Float16)1.f};
+      // P in fp16; l sums the same rounded values that enter the product,
+      // each fp16 half added to the fp32 sum by one v_fma_mix_f32 (x 1.0).
+      // Not v_dot2: it waits while the matrix core of its SIMD is busy,
+      // other VALU instructions do not.  The compiler makes a conversion
+      // and an add of each half, hence the asm.
       hi[w] = pack_f16x2(a, b);
-      l_run = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hi[w]), one, l_run, false);
+      asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(l_run) : "v"(hi[w]));
+      asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(l_run) : "v"(hi[w]));
     }
   };
   auto rescale_o = [&](float f) __attribute__((always_inline)) {
