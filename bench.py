@@ -36,22 +36,35 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s & achieved HBM GB/s (% of peak), 8B-GQA batch 256"
 # HBM bytes per launch of the dominant kernel of each workload, from two
 # rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each scaled by what the
-# counter reads for a device copy of known size), with the SHA-256 of the
-# kernel source they were taken on (profiles/traffic.json).  A figure is
-# reported only while the kernel source is unchanged; otherwise `traffic` is
-# null until the counters are taken again.
+# counter reads for a device copy of known size), with a digest of the kernel
+# code they were taken on (profiles/traffic.json).  A figure is reported only
+# while that code is unchanged; otherwise `traffic` is null until the counters
+# are taken again.
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_attention_06_amd", "csrc", "pkv_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def measured_traffic(key: str):
+def kernel_code_digest(path: str = KERNEL_SOURCE) -> str:
+    """SHA-256 of the kernel source without its comments, blank lines and
+    runs of blanks: edits of comments or layout keep the digest, any change
+    of code changes it.  (A `//` inside a string literal would count as a
+    comment; the kernel source has none.)"""
     import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    lines = [" ".join(line.split()) for line in text.split("\n")]
+    return hashlib.sha256("\n".join(line for line in lines if line).encode()).hexdigest()
+
+
+def measured_traffic(key: str):
     try:
         rec = json.load(open(TRAFFIC_FILE))[key]
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        digest = kernel_code_digest()
     except (OSError, KeyError, ValueError):
         return None
-    return int(rec["bytes_per_launch"]) if rec.get("kernel_source_sha256") == sha else None
+    return int(rec["bytes_per_launch"]) if rec.get("kernel_code_sha256") == digest else None
 
 
 def algorithmic_kv_bytes(w) -> int:

@@ -1955,7 +1955,7 @@ hipError_t launch_decode_rows(const CacheDesc& c, const AttnDesc& a, hipStream_t
 // zeroed.  The tile kernel keeps its accumulator in units of 2^kexp and
 // adjusts P or the accumulator by exact powers of two when a block's e
 // differs (all e are 0 unless some |v| >= 2^16).  The row sums l come from
-// the same rounded fp16 probabilities that enter the MFMA (v_dot2c_f32_f16,
+// the same rounded fp16 probabilities that enter the MFMA (v_fma_mix_f32,
 // before any such adjustment), so the normalisation matches the weights.
 //
 // One workgroup = 4 waves = one kv head x TQ positions; wave w takes query
