@@ -510,14 +510,15 @@ def run_prefix_cache(args):
     return {
         "metric": "host prefix caching: requests/s through match + append + register + release",
         "value": n_req / dt, "unit": "requests/s", "higher_is_better": True, "n_gpus": 1,
-        "steps": n_req, "warmup": 0, "ms_per_step": dt / n_req * 1e3, "dtype": "int32 token ids",
-        "data": "synthetic",
+        "steps": n_req, "warmup": 0, "ms_per_step": dt / n_req * 1e3, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32 token ids", "data": "synthetic",
         "config": {"workload": "requests sharing one 341-token prefix (21 full blocks) plus "
                                "16..400 tokens of their own; 256 alive; 200,000-block pool"},
         "block_hit_rate": hit_blocks / full_blocks,
         "prefill_tokens_saved": saved_tokens / all_tokens,
         "us_per_request": dt / n_req * 1e6,
-        "note": "host C++ through ctypes (the per-call ctypes marshalling is included)",
+        "note": "host C++ through ctypes (the per-call ctypes marshalling is included); a step "
+                "is one request, all 20,000 timed whatever --steps says",
     }
 
 

@@ -64,3 +64,28 @@ def test_committed_traffic_table_is_well_formed():
         assert int(rec["bytes_per_launch"]) > 0, key
         assert len(rec["kernel_code_sha256"]) == 64, key
         assert os.path.exists(os.path.join(ROOT, rec["profile"])), key
+
+
+def test_host_workload_prints_one_contract_line():
+    """The host-only prefix-cache workload runs without a GPU and prints one
+    JSON line with the fields every bench line carries."""
+    import subprocess
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "prefix-cache"],
+                         capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = [l for l in out.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1, lines
+    rec = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config"):
+        assert key in rec, key
+    assert rec["value"] > 0 and rec["n_gpus"] == 1 and "workload" in rec["config"]
+    assert 0.0 < rec["block_hit_rate"] < 1.0
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert out.returncode == 2
+    assert "one GPU" in json.loads(out.stdout.strip().splitlines()[-1])["error"]
