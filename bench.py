@@ -366,7 +366,7 @@ def run_mixed(args):
         "metric": "mixed chunked-prefill step: attention ms and prefill-tile MFMA TFLOP/s",
         "value": mixed["ms"], "unit": "ms", "higher_is_better": False,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mixed["ms"],
-        "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": mixed["workload"],
                    "flush_mb_read_before_each_step": args.flush_mb},
         "mixed_step": mixed, "prefill_chunk": prefill,
@@ -418,7 +418,7 @@ def run_prefill(args):
         "metric": "prefill chunk alone: MFMA TFLOP/s of the unmasked (query, key) pairs",
         "value": tflops, "unit": "TFLOP/s", "higher_is_better": True,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": mean,
-        "dtype": "bf16", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "flush_mb_read_before_each_step": args.flush_mb},
         "attention_ms_median": float(np.median(ms)),
         "items_q_tile_x_kv_head": items,
@@ -466,7 +466,7 @@ def run_swap(args):
         "metric": "block swap GB/s over the host link (swap out / swap in)",
         "value": gb_out, "unit": "GB/s", "higher_is_better": True, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": float(t_out.mean()),
-        "dtype": "bytes", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bytes", "data": "synthetic",
         "config": {"workload": f"8B GQA pool (64 KiB blocks): all {n} blocks of the 32 longest "
                                f"sequences ({nbytes / 2**20:.0f} MiB) to pinned host memory and back"},
         "swap_out_ms": float(t_out.mean()), "swap_in_ms": float(t_in.mean()),
